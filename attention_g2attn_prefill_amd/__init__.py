@@ -1,0 +1,18 @@
+"""Gemma 2 attention layer for MI355X (gfx950): prefill and decode.
+
+The compute path is the C-ABI library libg2attn.so (hand-written HIP kernels);
+this package is a thin ctypes binding over it plus a seeded input generator
+(`synth`).  The binding is loaded on first use of any entry point and raises
+if the library has not been built: there is no CPU fallback.
+"""
+_BINDING_NAMES = (
+    "prefill", "decode", "decode_workspace_bytes", "check_args", "status_string",
+    "library_path", "G2attnError", "lib",
+)
+
+
+def __getattr__(name):
+    if name in _BINDING_NAMES:
+        from . import _binding
+        return getattr(_binding, name)
+    raise AttributeError(name)

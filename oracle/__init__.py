@@ -1,0 +1,175 @@
+"""CPU fp64 oracle for the Gemma 2 attention layer (TEST INFRASTRUCTURE).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  It is the slow, plain definition the GPU kernels are checked
+against and shares no code with them (see g2_oracle.c for the definition and
+the passages it follows).
+
+Inputs are numpy arrays (or anything np.asarray accepts) that are converted to
+float32 without change of value (bf16 and fp32 inputs are exact in float32);
+results are float64.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libg2oracle.so")
+_lib = None
+
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_I = ctypes.c_int
+_D = ctypes.c_double
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _b
+        _b.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.g2o_softcap.argtypes = [_D, _D]
+    lib.g2o_softcap.restype = _D
+    lib.g2o_allowed.argtypes = [ctypes.c_int64, ctypes.c_int64, _I, _I]
+    lib.g2o_allowed.restype = _I
+    row_args = [_f32p, _f32p, _I, _I, _I, _I, _I, _I, _D, _D, _I, _I, _I, _I,
+                _I, _f64p]
+    lib.g2o_prefill_row_logits.argtypes = row_args
+    lib.g2o_prefill_row_logits.restype = _I
+    lib.g2o_prefill_row_weights.argtypes = row_args
+    lib.g2o_prefill_row_weights.restype = _I
+    lib.g2o_prefill.argtypes = [_f32p, _f32p, _f32p, _f64p, _I, _I, _I, _I, _I,
+                                _I, _D, _D, _I, _I, _i64p, ctypes.c_int64]
+    lib.g2o_prefill.restype = _I
+    lib.g2o_decode.argtypes = [_f32p, _f32p, _f32p, _i32p, _f64p, _I, _I, _I,
+                               _I, _I, _D, _D, _I, _I, _i64p, ctypes.c_int64]
+    lib.g2o_decode.restype = _I
+    _lib = lib
+    return lib
+
+
+def _f32(a):
+    a = np.asarray(a)
+    if a.dtype != np.float32:
+        a32 = a.astype(np.float32)
+        if not np.array_equal(a32.astype(a.dtype), a, equal_nan=True):
+            raise ValueError("oracle inputs must be exactly representable in float32")
+        a = a32
+    return np.ascontiguousarray(a)
+
+
+def _ptr(a, t):
+    return a.ctypes.data_as(t)
+
+
+class OracleError(ValueError):
+    pass
+
+
+def softcap(x, cap):
+    """cap * tanh(x / cap) in double; identity when cap <= 0 or cap = inf."""
+    lib = _load()
+    return lib.g2o_softcap(float(x), float(cap))
+
+
+def allowed(p, j, window, is_local):
+    """Mask predicate: can query position p see key position j."""
+    return bool(_load().g2o_allowed(int(p), int(j), int(window), int(bool(is_local))))
+
+
+def _shape_prefill(q, k, v):
+    B, T, H, d = q.shape
+    B2, S, KVH, d2 = k.shape
+    if (B2, d2) != (B, d) or v.shape != k.shape:
+        raise OracleError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
+    return B, T, S, H, KVH, d
+
+
+def row_logits(q, k, b, t, h, *, query_scale, softcap, window, is_local):
+    """Capped, masked logits of prefill row (b, t, h): float64 array of S."""
+    q, k = _f32(q), _f32(k)
+    B, T, H, d = q.shape
+    S, KVH = k.shape[1], k.shape[2]
+    out = np.empty(S, np.float64)
+    st = _load().g2o_prefill_row_logits(_ptr(q, _f32p), _ptr(k, _f32p), B, T, S, H,
+                                        KVH, d, query_scale, softcap, window,
+                                        int(bool(is_local)), b, t, h, _ptr(out, _f64p))
+    if st != 0:
+        raise OracleError(f"oracle rejected arguments (status {st})")
+    return out
+
+
+def row_weights(q, k, b, t, h, *, query_scale, softcap, window, is_local):
+    """Attention weights of prefill row (b, t, h): float64 array of S."""
+    q, k = _f32(q), _f32(k)
+    B, T, H, d = q.shape
+    S, KVH = k.shape[1], k.shape[2]
+    out = np.empty(S, np.float64)
+    st = _load().g2o_prefill_row_weights(_ptr(q, _f32p), _ptr(k, _f32p), B, T, S, H,
+                                         KVH, d, query_scale, softcap, window,
+                                         int(bool(is_local)), b, t, h, _ptr(out, _f64p))
+    if st != 0:
+        raise OracleError(f"oracle rejected arguments (status {st})")
+    return out
+
+
+def prefill(q, k, v, *, query_scale, softcap, window, is_local, rows=None):
+    """Attention output in float64.
+
+    q: (B,T,H,d); k, v: (B,S,KVH,d).  rows=None returns (B,T,H,d); otherwise
+    rows is a sequence of flat ids (b*T + t)*H + h and the result is (n, d).
+    """
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, T, S, H, KVH, d = _shape_prefill(q, k, v)
+    if rows is None:
+        out = np.empty((B, T, H, d), np.float64)
+        rp, n = None, 0
+    else:
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        out = np.empty((rows.size, d), np.float64)
+        rp, n = _ptr(rows, _i64p), rows.size
+    st = _load().g2o_prefill(_ptr(q, _f32p), _ptr(k, _f32p), _ptr(v, _f32p),
+                             _ptr(out, _f64p), B, T, S, H, KVH, d, query_scale,
+                             softcap, window, int(bool(is_local)), rp, n)
+    if st != 0:
+        raise OracleError(f"oracle rejected arguments (status {st})")
+    return out
+
+
+def decode(q, k_cache, v_cache, kv_lens, *, query_scale, softcap, window, is_local,
+           rows=None):
+    """Decode output in float64.
+
+    q: (B,1,H,d); caches: (B,S,KVH,d); kv_lens: (B,) ints >= 1.  Position j of
+    sequence b is read from slot j mod S.  rows=None returns (B,1,H,d);
+    otherwise rows are flat ids b*H + h and the result is (n, d).
+    """
+    q, kc, vc = _f32(q), _f32(k_cache), _f32(v_cache)
+    B, T, H, d = q.shape
+    if T != 1:
+        raise OracleError("decode takes one query token per sequence")
+    S, KVH = kc.shape[1], kc.shape[2]
+    if kc.shape[0] != B or kc.shape[3] != d or vc.shape != kc.shape:
+        raise OracleError("cache shape mismatch")
+    lens = np.ascontiguousarray(np.asarray(kv_lens, dtype=np.int32))
+    if lens.shape != (B,):
+        raise OracleError("kv_lens must have B entries")
+    if rows is None:
+        out = np.empty((B, 1, H, d), np.float64)
+        rp, n = None, 0
+    else:
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        out = np.empty((rows.size, d), np.float64)
+        rp, n = _ptr(rows, _i64p), rows.size
+    st = _load().g2o_decode(_ptr(q, _f32p), _ptr(kc, _f32p), _ptr(vc, _f32p),
+                            _ptr(lens, _i32p), _ptr(out, _f64p), B, S, H, KVH, d,
+                            query_scale, softcap, window, int(bool(is_local)), rp, n)
+    if st != 0:
+        raise OracleError(f"oracle rejected arguments (status {st})")
+    return out

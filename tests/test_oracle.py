@@ -1,0 +1,456 @@
+"""Pins of the CPU fp64 oracle against facts fixed by the pages and by mathematics.
+
+Each test checks the oracle against something other than itself: the golden
+mask of the Guide's demo layer, mpmath at 40 digits, a library attention routine
+(torch's scaled_dot_product_attention in float64 with the cap switched off),
+closed forms and invariants.  Chosen so that a dropped scale, a wrong tanh sign,
+a wrong head index, a transposed operand, an off-by-one window, a mask applied
+before the cap or a wrong causal alignment fails at least one test.
+"""
+import math
+
+import mpmath
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attention_g2attn_prefill_amd import synth
+
+mpmath.mp.dps = 40
+
+
+def rand(shape, seed, mul=1.0):
+    return synth.draw(shape, seed, 0, dtype="f32", mul=mul).numpy()
+
+
+def page_mask(T, S, window, is_local):
+    """Visibility built with torch.triu / torch.tril the way the Guide's demo
+    layer builds it (-inf above the diagonal; on sliding layers also at and below
+    offset -window), shifted so query row t sits at key column t + S - T."""
+    off = S - T
+    causal = torch.triu(torch.full((T, S), float("-inf"), dtype=torch.float64),
+                        diagonal=1 + off)
+    m = causal
+    if is_local:
+        m = m + torch.tril(torch.full((T, S), float("-inf"), dtype=torch.float64),
+                           diagonal=off - window)
+    return (m == 0).numpy()
+
+
+# --------------------------------------------------------------- mask and cap
+
+def test_mask_matches_guide_demo_golden(golden_dir):
+    rows = [ln.strip() for ln in open(f"{golden_dir}/mask_seq16_window4.txt")
+            if ln.strip() and not ln.startswith("#")]
+    gold = np.array([[c == "1" for c in r] for r in rows])
+    assert gold.shape == (16, 16)
+    got = np.array([[oracle.allowed(p, j, 4, True) for j in range(16)]
+                    for p in range(16)])
+    assert np.array_equal(got, gold)
+    # the oracle's logits put -inf exactly where the golden grid says masked
+    q = rand((1, 16, 1, 4), 11)
+    k = rand((1, 16, 1, 4), 12)
+    for t in range(16):
+        s = oracle.row_logits(q, k, 0, t, 0, query_scale=0.5, softcap=50.0,
+                              window=4, is_local=True)
+        assert np.array_equal(np.isfinite(s), gold[t])
+
+
+def test_global_mask_is_causal():
+    got = np.array([[oracle.allowed(p, j, 4, False) for j in range(16)]
+                    for p in range(16)])
+    assert np.array_equal(got, np.tril(np.ones((16, 16), bool)))
+
+
+@pytest.mark.parametrize("x", [0.0, 1e-8, -3.5, 12.25, 49.0, -50.0, 77.7,
+                               -300.0, 899.0, 2000.0, -1e6])
+def test_softcap_matches_mpmath(x):
+    cap = 50.0
+    ref = mpmath.mpf(cap) * mpmath.tanh(mpmath.mpf(x) / cap)
+    got = oracle.softcap(x, cap)
+    assert abs(mpmath.mpf(got) - ref) <= 4e-16 * max(1.0, abs(float(ref)))
+    assert abs(got) <= cap
+    if abs(x) < 900:
+        assert abs(got) < cap
+
+
+@pytest.mark.parametrize("cap", [0.0, -1.0, math.inf])
+def test_softcap_disabled_is_identity(cap):
+    for x in (-123.5, 0.0, 7.25, 1e5):
+        assert oracle.softcap(x, cap) == x
+
+
+def test_softcap_taylor_limit():
+    # cap*tanh(x/cap) = x - x^3/(3 cap^2) + ...: within |x|^3/(3cap^2) of x
+    cap = 1e4
+    for x in np.linspace(-20, 20, 41):
+        s = oracle.softcap(float(x), cap)
+        assert abs(s - x) <= abs(x) ** 3 / (3 * cap * cap) + 1e-15
+
+
+# ------------------------------------------------------- logits and weights
+
+def _mp_logits(q, k, b, t, h, qs, cap, window, is_local, G):
+    T, S = q.shape[1], k.shape[1]
+    p = t + S - T
+    g = h // G
+    out = []
+    for j in range(S):
+        if j > p or (is_local and not j > p - window):
+            out.append(None)
+            continue
+        x = mpmath.fsum(mpmath.mpf(float(q[b, t, h, e])) * qs *
+                        mpmath.mpf(float(k[b, j, g, e])) for e in range(q.shape[3]))
+        out.append(cap * mpmath.tanh(x / cap) if cap > 0 else x)
+    return out
+
+
+@pytest.mark.parametrize("is_local", [False, True])
+def test_row_logits_and_weights_match_mpmath(is_local):
+    B, T, S, H, KVH, d = 2, 9, 13, 4, 2, 8
+    q = rand((B, T, H, d), 21, mul=6.0)
+    k = rand((B, S, KVH, d), 22, mul=3.0)
+    qs, cap, W = 0.35, 50.0, 5
+    for (b, t, h) in [(0, 0, 0), (1, 8, 3), (0, 4, 1), (1, 2, 2)]:
+        ref = _mp_logits(q, k, b, t, h, mpmath.mpf(qs), mpmath.mpf(cap), W,
+                         is_local, H // KVH)
+        s = oracle.row_logits(q, k, b, t, h, query_scale=qs, softcap=cap,
+                              window=W, is_local=is_local)
+        w = oracle.row_weights(q, k, b, t, h, query_scale=qs, softcap=cap,
+                               window=W, is_local=is_local)
+        live = [r for r in ref if r is not None]
+        m = max(live)
+        z = mpmath.fsum(mpmath.exp(r - m) for r in live)
+        for j, r in enumerate(ref):
+            if r is None:
+                assert s[j] == -math.inf and w[j] == 0.0
+            else:
+                assert abs(s[j] - float(r)) <= 1e-13 * max(1.0, abs(float(r)))
+                assert abs(w[j] - float(mpmath.exp(r - m) / z)) <= 1e-14
+        assert abs(w.sum() - 1.0) <= 1e-14
+
+
+def test_capped_logits_are_bounded():
+    q = rand((1, 64, 2, 16), 31, mul=40.0)
+    k = rand((1, 64, 1, 16), 32, mul=40.0)
+    xs = []
+    for t in range(0, 64, 7):
+        s = oracle.row_logits(q, k, 0, t, 1, query_scale=0.25, softcap=50.0,
+                              window=64, is_local=False)
+        f = s[np.isfinite(s)]
+        assert np.all(np.abs(f) <= 50.0)
+        raw = oracle.row_logits(q, k, 0, t, 1, query_scale=0.25, softcap=0.0,
+                                window=64, is_local=False)
+        xs.append(np.abs(raw[np.isfinite(raw)]).max())
+    assert max(xs) > 100.0  # the check saw logits far beyond the cap
+
+
+# ------------------------------------------------ library routine (cap off)
+
+def _sdpa(q, k, v, qs, window, is_local):
+    B, T, H, d = q.shape
+    S, KVH = k.shape[1], k.shape[2]
+    G = H // KVH
+    qt = torch.from_numpy(q.astype(np.float64)).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(k.astype(np.float64)).permute(0, 2, 1, 3)
+    vt = torch.from_numpy(v.astype(np.float64)).permute(0, 2, 1, 3)
+    kt = kt.repeat_interleave(G, dim=1)
+    vt = vt.repeat_interleave(G, dim=1)
+    mask = torch.from_numpy(page_mask(T, S, window, is_local))
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask,
+                                                         scale=qs)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+@pytest.mark.parametrize("T,S", [(37, 37), (7, 37), (1, 20)])
+@pytest.mark.parametrize("is_local,window", [(False, 1), (True, 5), (True, 1),
+                                             (True, 40)])
+@pytest.mark.parametrize("H,KVH", [(4, 2), (6, 6), (4, 1)])
+def test_cap_off_matches_library_attention(T, S, is_local, window, H, KVH):
+    B, d = 2, 16
+    q = rand((B, T, H, d), 41)
+    k = rand((B, S, KVH, d), 42)
+    v = rand((B, S, KVH, d), 43)
+    qs = 0.3
+    for cap in (0.0, math.inf):
+        got = oracle.prefill(q, k, v, query_scale=qs, softcap=cap, window=window,
+                             is_local=is_local)
+        ref = _sdpa(q, k, v, qs, window, is_local)
+        assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def test_large_cap_approaches_plain_attention():
+    B, T, H, KVH, d = 1, 24, 2, 1, 8
+    q = rand((B, T, H, d), 51)
+    k = rand((B, T, KVH, d), 52)
+    v = rand((B, T, KVH, d), 53)
+    qs, cap = 0.5, 1e4
+    capped = oracle.prefill(q, k, v, query_scale=qs, softcap=cap, window=4, is_local=True)
+    plain = _sdpa(q, k, v, qs, 4, True)
+    xmax = max(np.abs(oracle.row_logits(q, k, 0, t, h, query_scale=qs, softcap=0.0,
+                                        window=4, is_local=True)[np.isfinite(
+        oracle.row_logits(q, k, 0, t, h, query_scale=qs, softcap=0.0, window=4,
+                          is_local=True))]).max() for t in range(T) for h in range(H))
+    dlogit = xmax ** 3 / (3 * cap * cap)
+    # each weight moves by at most a factor exp(+-2 dlogit)
+    bound = 4 * dlogit * np.abs(v).max() + 1e-12
+    assert np.max(np.abs(capped - plain)) <= bound
+    assert np.max(np.abs(capped - plain)) > 0.0
+
+
+# ------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("is_local,window", [(False, 1), (True, 1), (True, 3),
+                                             (True, 16), (True, 30)])
+def test_zero_query_gives_window_mean(is_local, window):
+    B, T, H, KVH, d = 2, 20, 4, 2, 6
+    q = np.zeros((B, T, H, d), np.float32)
+    k = rand((B, T, KVH, d), 61)
+    v = rand((B, T, KVH, d), 62)
+    out = oracle.prefill(q, k, v, query_scale=0.7, softcap=50.0, window=window,
+                         is_local=is_local)
+    v64 = v.astype(np.float64)
+    for b in range(B):
+        for t in range(T):
+            lo = max(0, t - window + 1) if is_local else 0
+            for h in range(H):
+                ref = v64[b, lo:t + 1, h // 2].mean(axis=0)
+                assert np.max(np.abs(out[b, t, h] - ref)) <= 1e-14
+
+
+def test_window_one_returns_own_value():
+    q = rand((2, 11, 4, 8), 71, mul=5.0)
+    k = rand((2, 11, 2, 8), 72)
+    v = rand((2, 11, 2, 8), 73)
+    out = oracle.prefill(q, k, v, query_scale=0.3, softcap=50.0, window=1, is_local=True)
+    for h in range(4):
+        assert np.array_equal(out[:, :, h], v[:, :, h // 2].astype(np.float64))
+
+
+@pytest.mark.parametrize("is_local", [False, True])
+def test_first_row_returns_first_value(is_local):
+    q = rand((3, 9, 2, 8), 81, mul=9.0)
+    k = rand((3, 9, 1, 8), 82)
+    v = rand((3, 9, 1, 8), 83)
+    out = oracle.prefill(q, k, v, query_scale=1.0, softcap=50.0, window=3,
+                         is_local=is_local)
+    for h in range(2):
+        assert np.array_equal(out[:, 0, h], v[:, 0, 0].astype(np.float64))
+
+
+def test_window_at_least_T_equals_global():
+    q = rand((1, 33, 4, 8), 91, mul=4.0)
+    k = rand((1, 33, 2, 8), 92)
+    v = rand((1, 33, 2, 8), 93)
+    g = oracle.prefill(q, k, v, query_scale=0.4, softcap=50.0, window=1, is_local=False)
+    for W in (33, 34, 1000):
+        loc = oracle.prefill(q, k, v, query_scale=0.4, softcap=50.0, window=W,
+                             is_local=True)
+        assert np.array_equal(loc, g)
+    loc = oracle.prefill(q, k, v, query_scale=0.4, softcap=50.0, window=32, is_local=True)
+    assert not np.array_equal(loc, g)
+
+
+def test_gqa_equals_repeated_heads():
+    q = rand((2, 15, 8, 8), 101, mul=3.0)
+    k = rand((2, 15, 4, 8), 102)
+    v = rand((2, 15, 4, 8), 103)
+    for is_local in (False, True):
+        a = oracle.prefill(q, k, v, query_scale=0.5, softcap=50.0, window=4,
+                           is_local=is_local)
+        kr = np.repeat(k, 2, axis=2)
+        vr = np.repeat(v, 2, axis=2)
+        m = oracle.prefill(q, kr, vr, query_scale=0.5, softcap=50.0, window=4,
+                           is_local=is_local)
+        assert np.array_equal(a, m)
+
+
+def test_constant_values_pass_through():
+    q = rand((1, 12, 2, 8), 111, mul=10.0)
+    k = rand((1, 12, 1, 8), 112)
+    c = np.linspace(-2, 3, 8).astype(np.float32)
+    v = np.broadcast_to(c, (1, 12, 1, 8)).copy()
+    out = oracle.prefill(q, k, v, query_scale=0.9, softcap=50.0, window=5, is_local=True)
+    assert np.max(np.abs(out - c.astype(np.float64))) <= 1e-14
+
+
+def test_two_key_row_is_logistic_mix():
+    q = rand((1, 2, 1, 4), 121, mul=8.0)
+    k = rand((1, 2, 1, 4), 122, mul=8.0)
+    v = rand((1, 2, 1, 4), 123)
+    qs, cap = 0.5, 50.0
+    out = oracle.prefill(q, k, v, query_scale=qs, softcap=cap, window=2, is_local=False)
+    s = [cap * mpmath.tanh(mpmath.fsum(mpmath.mpf(float(q[0, 1, 0, e])) * qs *
+                                       mpmath.mpf(float(k[0, j, 0, e]))
+                                       for e in range(4)) / cap) for j in range(2)]
+    w1 = 1 / (1 + mpmath.exp(s[0] - s[1]))
+    w0 = 1 / (1 + mpmath.exp(s[1] - s[0]))
+    ref = [float(w1 * float(v[0, 1, 0, e]) + w0 * float(v[0, 0, 0, e])) for e in range(4)]
+    assert np.max(np.abs(out[0, 1, 0] - np.array(ref))) <= 1e-15
+
+
+def test_saturated_logits_closed_form():
+    # key 0 at x = +2000, the other n-1 keys at x = -2000: s = +-50 exactly
+    n, d = 10, 2
+    q = np.zeros((1, n, 1, d), np.float32)
+    q[0, n - 1, 0, 0] = 40.0
+    k = np.zeros((1, n, 1, d), np.float32)
+    k[0, :, 0, 0] = -50.0
+    k[0, 0, 0, 0] = 50.0
+    v = rand((1, n, 1, d), 131)
+    out = oracle.prefill(q, k, v, query_scale=1.0, softcap=50.0, window=n, is_local=False)
+    s = oracle.row_logits(q, k, 0, n - 1, 0, query_scale=1.0, softcap=50.0, window=n,
+                          is_local=False)
+    assert s[0] == 50.0 and np.all(s[1:] == -50.0)
+    e = math.exp(-100.0)
+    vm = v[0, 1:, 0].astype(np.float64).mean(axis=0)
+    ref = (v[0, 0, 0].astype(np.float64) + (n - 1) * e * vm) / (1 + (n - 1) * e)
+    assert np.max(np.abs(out[0, n - 1, 0] - ref)) <= 1e-15
+
+
+def test_cap_is_applied_before_the_mask():
+    # Every visible key has x = -2000 (s = -50).  Masked keys have x = +2000.
+    # Capping first and then masking gives them weight 0, so the output is the
+    # plain mean of the visible values; masking first and capping -inf to -50
+    # would give masked keys the same weight as visible ones.
+    T, d, W = 12, 2, 3
+    q = np.zeros((1, T, 1, d), np.float32)
+    q[0, :, 0, 0] = 40.0
+    k = np.zeros((1, T, 1, d), np.float32)
+    k[0, :, 0, 0] = -50.0
+    k[0, 0:T:2, 0, 0] = 50.0  # even positions: large positive logits
+    v = rand((1, T, 1, d), 141)
+    out = oracle.prefill(q, k, v, query_scale=1.0, softcap=50.0, window=W, is_local=True)
+    for t in range(T):
+        lo = max(0, t - W + 1)
+        vis = list(range(lo, t + 1))
+        s = np.array([50.0 if j % 2 == 0 else -50.0 for j in vis])
+        w = np.exp(s - s.max())
+        w /= w.sum()
+        ref = (w[:, None] * v[0, vis, 0].astype(np.float64)).sum(axis=0)
+        assert np.max(np.abs(out[0, t, 0] - ref)) <= 1e-14
+
+
+def test_linearity_in_values():
+    q = rand((1, 17, 2, 8), 151, mul=4.0)
+    k = rand((1, 17, 1, 8), 152)
+    v1 = rand((1, 17, 1, 8), 153)
+    v2 = rand((1, 17, 1, 8), 154)
+    a, b = 0.75, -1.5
+    kw = dict(query_scale=0.5, softcap=50.0, window=6, is_local=True)
+    o1 = oracle.prefill(q, k, v1, **kw)
+    o2 = oracle.prefill(q, k, v2, **kw)
+    # round the combination to float32 and use the exact float32 value as input
+    vc = (np.float32(a) * v1 + np.float32(b) * v2)
+    dv = vc.astype(np.float64) - (a * v1.astype(np.float64) + b * v2.astype(np.float64))
+    o = oracle.prefill(q, k, vc, **kw)
+    bound = 1e-13 + np.abs(dv).max()
+    assert np.max(np.abs(o - (a * o1 + b * o2))) <= bound
+
+
+# ------------------------------------------------------------------- decode
+
+@pytest.mark.parametrize("is_local", [False, True])
+def test_decode_equals_last_prefill_row(is_local):
+    B, S, H, KVH, d, W = 3, 40, 4, 2, 8, 7
+    q = rand((B, 1, H, d), 161, mul=3.0)
+    kc = rand((B, S, KVH, d), 162)
+    vc = rand((B, S, KVH, d), 163)
+    lens = np.array([1, 17, 40], np.int32)
+    got = oracle.decode(q, kc, vc, lens, query_scale=0.4, softcap=50.0, window=W,
+                        is_local=is_local)
+    for b in range(B):
+        L = int(lens[b])
+        ref = oracle.prefill(q[b:b + 1], kc[b:b + 1, :L], vc[b:b + 1, :L],
+                             query_scale=0.4, softcap=50.0, window=W, is_local=is_local)
+        assert np.array_equal(got[b, 0], ref[0, 0])
+
+
+@pytest.mark.parametrize("lens", [[13, 50, 64, 200], [1, 3, 8, 9]])
+def test_decode_ring_equals_linear_cache(lens):
+    B, S, H, KVH, d, W = 4, 200, 4, 2, 8, 8
+    q = torch.from_numpy(rand((B, 1, H, d), 171, mul=3.0))
+    kc = torch.from_numpy(rand((B, S, KVH, d), 172))
+    vc = torch.from_numpy(rand((B, S, KVH, d), 173))
+    lens = np.array(lens, np.int32)
+    kr = synth.ring_from_linear(kc, lens, W)
+    vr = synth.ring_from_linear(vc, lens, W)
+    lin = oracle.decode(q.numpy(), kc.numpy(), vc.numpy(), lens, query_scale=0.4,
+                        softcap=50.0, window=W, is_local=True)
+    ring = oracle.decode(q.numpy(), kr.numpy(), vr.numpy(), lens, query_scale=0.4,
+                         softcap=50.0, window=W, is_local=True)
+    assert np.all(np.isfinite(ring))  # NaN-filled unused slots never read
+    assert np.max(np.abs(ring - lin)) <= 1e-14
+
+
+def test_decode_partial_ring_equals_global_prefix():
+    B, H, KVH, d, W = 2, 2, 1, 8, 16
+    q = torch.from_numpy(rand((B, 1, H, d), 181, mul=2.0))
+    kc = torch.from_numpy(rand((B, 40, KVH, d), 182))
+    vc = torch.from_numpy(rand((B, 40, KVH, d), 183))
+    lens = np.array([5, 16], np.int32)
+    kr = synth.ring_from_linear(kc, lens, W)
+    vr = synth.ring_from_linear(vc, lens, W)
+    loc = oracle.decode(q.numpy(), kr.numpy(), vr.numpy(), lens, query_scale=0.5,
+                        softcap=50.0, window=W, is_local=True)
+    glob = oracle.decode(q.numpy(), kc.numpy(), vc.numpy(), lens, query_scale=0.5,
+                         softcap=50.0, window=W, is_local=False)
+    assert np.max(np.abs(loc - glob)) <= 1e-14
+
+
+def test_decode_rejects_unreachable_positions():
+    q = rand((1, 1, 2, 4), 191)
+    kc = rand((1, 8, 1, 4), 192)
+    with pytest.raises(oracle.OracleError):
+        oracle.decode(q, kc, kc, np.array([9], np.int32), query_scale=1.0, softcap=50.0,
+                      window=8, is_local=False)
+    with pytest.raises(oracle.OracleError):
+        oracle.decode(q, kc, kc, np.array([0], np.int32), query_scale=1.0, softcap=50.0,
+                      window=8, is_local=False)
+    # a local layer with window <= S may hold any number of tokens (ring)
+    oracle.decode(q, kc, kc, np.array([100], np.int32), query_scale=1.0, softcap=50.0,
+                  window=8, is_local=True)
+
+
+def test_rows_subset_matches_full():
+    q = rand((2, 10, 4, 8), 201, mul=2.0)
+    k = rand((2, 10, 2, 8), 202)
+    v = rand((2, 10, 2, 8), 203)
+    full = oracle.prefill(q, k, v, query_scale=0.4, softcap=50.0, window=3, is_local=True)
+    rows = [0, 5, 79, 33]
+    part = oracle.prefill(q, k, v, query_scale=0.4, softcap=50.0, window=3, is_local=True,
+                          rows=rows)
+    assert np.array_equal(part, full.reshape(-1, 8)[rows])
+
+
+# ---------------------------------------------------------------- brute force
+
+def test_brute_force_mpmath_tiny():
+    """Every output element of a tiny layer recomputed at 40 digits with the
+    mask taken from the Guide-style triu/tril construction."""
+    B, T, S, H, KVH, d, W = 1, 6, 6, 2, 1, 3, 2
+    q = rand((B, T, H, d), 211, mul=20.0)
+    k = rand((B, S, KVH, d), 212, mul=3.0)
+    v = rand((B, S, KVH, d), 213)
+    qs, cap = 0.75, 50.0
+    for is_local in (False, True):
+        mask = page_mask(T, S, W, is_local)
+        out = oracle.prefill(q, k, v, query_scale=qs, softcap=cap, window=W,
+                             is_local=is_local)
+        for t in range(T):
+            for h in range(H):
+                qv = [mpmath.mpf(float(x)) * mpmath.mpf(qs) for x in q[0, t, h]]
+                s = {}
+                for j in range(S):
+                    if mask[t, j]:
+                        x = mpmath.fsum(qv[e] * mpmath.mpf(float(k[0, j, 0, e]))
+                                        for e in range(d))
+                        s[j] = cap * mpmath.tanh(x / cap)
+                m = max(s.values())
+                z = mpmath.fsum(mpmath.exp(x - m) for x in s.values())
+                for e in range(d):
+                    ref = mpmath.fsum(mpmath.exp(s[j] - m) / z * mpmath.mpf(float(v[0, j, 0, e]))
+                                      for j in s)
+                    # logits near the cap carry ~ulp(50) = 7e-15 absolute error in fp64
+                    assert abs(out[0, t, h, e] - float(ref)) <= 2e-14
