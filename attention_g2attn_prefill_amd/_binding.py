@@ -1,0 +1,133 @@
+"""ctypes binding of libg2attn.so: argument marshalling only.
+
+Every step of prefill and decode runs in the library's HIP kernels; torch
+provides device memory and the current HIP stream.  There is no fallback: if
+the library is missing, importing this module raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libg2attn.so")
+
+if not os.path.exists(library_path):
+    raise ImportError(
+        f"{library_path} is not built; run `python -m attention_g2attn_prefill_amd.build` "
+        "(or __graft_entry__.build()) first")
+
+lib = ctypes.CDLL(library_path)
+
+_vp = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+
+lib.g2attn_prefill.argtypes = [_vp, _vp, _vp, _vp, _I, _I, _I, _I, _I, _I, _F, _F, _I, _I,
+                               _I, _vp]
+lib.g2attn_prefill.restype = _I
+lib.g2attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _I, _I, _I, _I, _I, _I, _F, _F, _I,
+                              _I, _I, _vp, ctypes.c_size_t, _vp]
+lib.g2attn_decode.restype = _I
+lib.g2attn_decode_workspace_bytes.argtypes = [_I, _I, _I, _I]
+lib.g2attn_decode_workspace_bytes.restype = ctypes.c_size_t
+lib.g2attn_check_args.argtypes = [_I] * 10
+lib.g2attn_check_args.restype = _I
+lib.g2attn_status_string.argtypes = [_I]
+lib.g2attn_status_string.restype = ctypes.c_char_p
+
+G2_BF16, G2_F32 = 0, 1
+_DTYPES = {torch.bfloat16: G2_BF16, torch.float32: G2_F32}
+
+
+class G2attnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def status_string(status: int) -> str:
+    return lib.g2attn_status_string(int(status)).decode()
+
+
+def check_args(B, T, S, H, KVH, d, window, is_local, dtype=G2_BF16, decode=False) -> int:
+    """Host-only validation; returns the status the call would return."""
+    return lib.g2attn_check_args(B, T, S, H, KVH, d, window, int(is_local), dtype,
+                                 int(bool(decode)))
+
+
+def decode_workspace_bytes(B, H, d, S) -> int:
+    return int(lib.g2attn_decode_workspace_bytes(B, H, d, S))
+
+
+def _stream_handle(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def prefill(q, k, v, *, query_scale, softcap=50.0, window=4096, is_local, out=None,
+            stream=None):
+    """Soft-capped GQA attention for a prefill: q (B,T,H,d), k/v (B,S,KVH,d).
+
+    Returns out (B,T,H,d) in q's dtype.  Enqueued on `stream` (default: the
+    current stream); the call does not synchronise.
+    """
+    B, T, H, d = q.shape
+    Bk, S, KVH, dk = k.shape
+    if (Bk, dk) != (B, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch: q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share dtype bfloat16 or float32")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q's shape and dtype")
+    st = lib.g2attn_prefill(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+                            B, T, S, H, KVH, d, float(query_scale), float(softcap),
+                            int(window), int(bool(is_local)), _DTYPES[q.dtype],
+                            _stream_handle(stream))
+    if st != 0:
+        raise G2attnError(st, "g2attn_prefill")
+    return out
+
+
+def decode(q, k_cache, v_cache, kv_lens, *, query_scale, softcap=50.0, window=4096,
+           is_local, out=None, workspace=None, stream=None):
+    """One query token per sequence against a KV cache.
+
+    q (B,1,H,d); k_cache/v_cache (B,S,KVH,d) with position j in slot j mod S;
+    kv_lens int32 (B,) on the GPU.  workspace: a uint8 GPU tensor of at least
+    decode_workspace_bytes(B,H,d,S) bytes (allocated here if None).
+    """
+    B, T, H, d = q.shape
+    Bk, S, KVH, dk = k_cache.shape
+    if (Bk, dk) != (B, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("shape mismatch between q and the caches")
+    if q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and caches must share dtype bfloat16 or float32")
+    if kv_lens.dtype != torch.int32 or tuple(kv_lens.shape) != (B,):
+        raise TypeError("kv_lens must be int32 of shape (B,)")
+    need = decode_workspace_bytes(B, H, d, S)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q's shape and dtype")
+    st = lib.g2attn_decode(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                           _dev(out, "out"), _dev(kv_lens, "kv_lens"), B, T, S, H, KVH, d,
+                           float(query_scale), float(softcap), int(window),
+                           int(bool(is_local)), _DTYPES[q.dtype], _dev(workspace, "workspace"),
+                           workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    if st != 0:
+        raise G2attnError(st, "g2attn_decode")
+    return out

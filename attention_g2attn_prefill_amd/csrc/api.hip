@@ -1,0 +1,88 @@
+// C-ABI entry points of libg2attn (declared in include/g2attn.h).
+//
+// Host side only: argument validation (the same checks g2attn_check_args
+// exposes to CPU-only callers), dispatch on (dtype, head dim, heads per K/V
+// head) and launch on the caller's stream.  No allocation, no global state.
+#include <stdint.h>
+
+#include "g2_kernels.h"
+#include "g2attn.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_scalars(int B, int T, int S, int H, int KVH, int d, int window, int is_local,
+                  int dtype, int decode) {
+  if (B <= 0 || T <= 0 || S <= 0 || H <= 0 || KVH <= 0 || d <= 0) return G2_ERR_ARG;
+  if (dtype != G2_BF16 && dtype != G2_F32) return G2_ERR_ARG;
+  if (H % KVH != 0) return G2_ERR_ARG;
+  if (T > S) return G2_ERR_ARG;
+  if (is_local != 0 && is_local != 1) return G2_ERR_ARG;
+  if (is_local && window < 1) return G2_ERR_ARG;
+  if (decode && T != 1) return G2_ERR_ARG;
+  if (d != 64 && d != 128 && d != 256) return G2_ERR_UNSUPPORTED;
+  const int G = H / KVH;
+  if (G != 1 && G != 2) return G2_ERR_UNSUPPORTED;
+  // Index arithmetic inside the kernels is 32-bit per (batch, head) slice.
+  if ((long long)S * KVH * d >= (1LL << 31) || (long long)T * H * d >= (1LL << 31)) return G2_ERR_UNSUPPORTED;
+  return G2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int g2attn_check_args(int B, int T, int S, int H, int KVH, int d, int window, int is_local,
+                      int dtype, int decode) {
+  return check_scalars(B, T, S, H, KVH, d, window, is_local, dtype, decode);
+}
+
+const char* g2attn_status_string(int status) {
+  switch (status) {
+    case G2_OK: return "ok";
+    case G2_ERR_ARG: return "invalid argument";
+    case G2_ERR_UNSUPPORTED: return "unsupported shape (d must be 64, 128 or 256; H/KVH 1 or 2)";
+    case G2_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case G2_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case G2_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t g2attn_decode_workspace_bytes(int B, int H, int d, int S) {
+  if (B <= 0 || H <= 0 || d <= 0 || S <= 0) return 0;
+  return g2::decode_workspace_bytes(B, H, d, S);
+}
+
+int g2attn_prefill(const void* q, const void* k, const void* v, void* out, int B, int T, int S,
+                   int H, int KVH, int d, float query_scale, float softcap, int window,
+                   int is_local, int dtype, hipStream_t stream) {
+  int st = check_scalars(B, T, S, H, KVH, d, window, is_local, dtype, 0);
+  if (st != G2_OK) return st;
+  if (!q || !k || !v || !out) return G2_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return G2_ERR_ALIGN;
+  g2::PrefillLaunch L{q, k, v, out, B, T, S, H, KVH, d, query_scale, softcap, window, is_local};
+  const hipError_t e = dtype == G2_BF16 ? g2::launch_prefill_bf16(L, stream)
+                                        : g2::launch_prefill_f32(L, stream);
+  return e == hipSuccess ? G2_OK : G2_ERR_LAUNCH;
+}
+
+int g2attn_decode(const void* q, const void* k_cache, const void* v_cache, void* out,
+                  const int32_t* kv_lens, int B, int T, int S, int H, int KVH, int d,
+                  float query_scale, float softcap, int window, int is_local, int dtype,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_scalars(B, T, S, H, KVH, d, window, is_local, dtype, 1);
+  if (st != G2_OK) return st;
+  if (!q || !k_cache || !v_cache || !out || !kv_lens) return G2_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return G2_ERR_ALIGN;
+  if (!workspace || workspace_bytes < g2::decode_workspace_bytes(B, H, d, S)) return G2_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return G2_ERR_ALIGN;
+  g2::DecodeLaunch L{q, k_cache, v_cache, out, kv_lens, B, S, H, KVH, d,
+                     query_scale, softcap, window, is_local, workspace};
+  const hipError_t e = g2::launch_decode(L, dtype, stream);
+  return e == hipSuccess ? G2_OK : G2_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,303 @@
+// Decode: one new query token per sequence against a KV cache, split over the
+// keys (split-K) and merged with a log-sum-exp combine.
+//
+// Gemma 2 keeps only the last 4096 tokens on local layers (Guide, section 2;
+// model card "Method" item 1).  Position j of a sequence lives in cache slot
+// j mod S, so a local cache of S = 4096 slots is a ring and a global cache is
+// linear; the query of a sequence holding L tokens sits at position L - 1.
+//
+// The work is HBM-bound (each visible key costs 4*d bytes of K and V for
+// 8*d flops per query-head pair), so the kernel is built around the loads:
+//  * a workgroup (4 waves) owns kDecodeChunk consecutive positions of one
+//    (sequence, K/V head); both query heads of the pair reuse every K/V byte;
+//  * a key row is read by a group of d/8 lanes with 16-byte loads (d=256:
+//    half a wave per 512-byte row), so every load instruction is coalesced;
+//  * each lane group keeps 4 keys' loads in flight and its own online-softmax
+//    state; logits are reduced across the group with lane shuffles;
+//  * groups, then waves (through LDS), are merged at the end, and each split
+//    writes (max, sum, unnormalised accumulator) to the workspace;
+//  * a second kernel merges the splits of every (sequence, head).
+#include "g2_device.h"
+#include "g2_kernels.h"
+
+namespace g2 {
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  const int32_t* kv_lens;
+  int B, S, H, KVH;
+  CapConsts cap;
+  int window, is_local, nsplit;
+  float* ws_m;
+  float* ws_l;
+  float* ws_acc;
+};
+
+template <typename E>
+struct Vec16;
+template <>
+struct Vec16<bf16> {
+  static constexpr int N = 8;
+  __device__ static void load(const bf16* p, float (&x)[8]) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_lo_to_f32(w[i]);
+      x[2 * i + 1] = bf16_hi_to_f32(w[i]);
+    }
+  }
+};
+template <>
+struct Vec16<float> {
+  static constexpr int N = 4;
+  __device__ static void load(const float* p, float (&x)[4]) {
+    const f32x4 w = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = w[i];
+  }
+};
+
+__device__ __forceinline__ bool decode_len_ok(int L, int S, int window, int is_local) {
+  if (L < 1) return false;
+  const int seen = is_local ? min(L, window) : L;
+  return seen <= S;
+}
+
+template <typename E, int D, int G>
+__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+  constexpr int VEC = Vec16<E>::N;
+  constexpr int LPK = D / VEC;   // lanes per key row
+  constexpr int KPI = 64 / LPK;  // keys per wave step
+  constexpr int UNR = 4;         // keys in flight per lane group
+  static_assert(LPK <= 64 && 64 % LPK == 0, "key row must fit a wave");
+
+  __shared__ float sm_m[4][G], sm_l[4][G];
+  __shared__ float sm_acc[4][G][D];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = lane / LPK, sub = lane % LPK;
+  const int split = blockIdx.x;
+  const int bg = blockIdx.y;
+  const int b = bg / a.KVH, g = bg % a.KVH;
+  const int S = a.S;
+  const int L = a.kv_lens[b];
+  const bool ok = decode_len_ok(L, S, a.window, a.is_local);
+  const int lo = a.is_local ? max(0, L - a.window) : 0;
+  const int c0 = lo + split * kDecodeChunk;
+  const int c1 = min(c0 + kDecodeChunk, L);
+  const size_t part0 = ((size_t)b * a.H + (size_t)g * G) * a.nsplit + split;  // head g*G
+  if (!ok || c0 >= c1) {
+    if (tid < G) {
+      a.ws_m[part0 + (size_t)tid * a.nsplit] = kNegInf;
+      a.ws_l[part0 + (size_t)tid * a.nsplit] = 0.f;
+    }
+    return;
+  }
+
+  const E* qbase = static_cast<const E*>(a.q) + ((size_t)b * a.H + (size_t)g * G) * D + sub * VEC;
+  float qv[G][VEC];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) Vec16<E>::load(qbase + hh * D, qv[hh]);
+
+  const size_t row_stride = (size_t)a.KVH * D;
+  const E* kb = static_cast<const E*>(a.k) + ((size_t)b * S * a.KVH + g) * D + sub * VEC;
+  const E* vb = static_cast<const E*>(a.v) + ((size_t)b * S * a.KVH + g) * D + sub * VEC;
+
+  float m[G], l[G], acc[G][VEC];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    m[hh] = kNegInf;
+    l[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[hh][e] = 0.f;
+  }
+
+  const int c0_slot = c0 % S;
+  constexpr int kStep = 4 * KPI * UNR;  // positions per workgroup step
+  for (int base = c0 + wave * KPI * UNR; base < c1; base += kStep) {
+    float kx[UNR][VEC], vx[UNR][VEC];
+    bool in[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int pos = base + u * KPI + grp;
+      in[u] = pos < c1;
+      int slot = c0_slot + (pos - c0);
+      if (slot >= S) slot -= S;
+      if (in[u]) {
+        Vec16<E>::load(kb + (size_t)slot * row_stride, kx[u]);
+        Vec16<E>::load(vb + (size_t)slot * row_stride, vx[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) kx[u][e] = vx[u][e] = 0.f;
+      }
+    }
+    float s2[UNR][G];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u)
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) d = __builtin_fmaf(qv[hh][e], kx[u][e], d);
+#pragma unroll
+        for (int mk = LPK / 2; mk >= 1; mk >>= 1) d += shfl_xor(d, mk);
+        const float s = capped_log2(a.cap.mode, d, a.cap.k_in, a.cap.c_out);
+        s2[u][hh] = in[u] ? s : kNegInf;
+      }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float mb = s2[0][hh];
+#pragma unroll
+      for (int u = 1; u < UNR; ++u) mb = fmaxf(mb, s2[u][hh]);
+      const float m_new = fmaxf(m[hh], mb);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = exp2_fast(m[hh] - m_use);
+      float p[UNR];
+      float ps = 0.f;
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        p[u] = exp2_fast(s2[u][hh] - m_use);
+        ps += p[u];
+      }
+      l[hh] = l[hh] * alpha + ps;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        float x = acc[hh][e] * alpha;
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) x = __builtin_fmaf(p[u], vx[u][e], x);
+        acc[hh][e] = x;
+      }
+      m[hh] = m_new;
+    }
+  }
+
+  // ---- merge the KPI lane groups of this wave
+#pragma unroll
+  for (int step = LPK; step < 64; step <<= 1) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float mo = shfl_xor(m[hh], step);
+      const float lo_ = shfl_xor(l[hh], step);
+      const float mn = fmaxf(m[hh], mo);
+      const float mu = (mn == kNegInf) ? 0.f : mn;
+      const float fa = exp2_fast(m[hh] - mu), fb = exp2_fast(mo - mu);
+      l[hh] = l[hh] * fa + lo_ * fb;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float ao = shfl_xor(acc[hh][e], step);
+        acc[hh][e] = acc[hh][e] * fa + ao * fb;
+      }
+      m[hh] = mn;
+    }
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      if (sub == 0) {
+        sm_m[wave][hh] = m[hh];
+        sm_l[wave][hh] = l[hh];
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) sm_acc[wave][hh][sub * VEC + e] = acc[hh][e];
+    }
+  }
+  __syncthreads();
+  // ---- merge the 4 waves and write this split's partial result
+  for (int i = tid; i < G * D; i += 256) {
+    const int hh = i / D, dd = i % D;
+    float mn = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mn = fmaxf(mn, sm_m[w][hh]);
+    const float mu = (mn == kNegInf) ? 0.f : mn;
+    float ls = 0.f, as = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = exp2_fast(sm_m[w][hh] - mu);
+      ls += sm_l[w][hh] * f;
+      as += sm_acc[w][hh][dd] * f;
+    }
+    const size_t pi = part0 + (size_t)hh * a.nsplit;
+    a.ws_acc[pi * D + dd] = as;
+    if (dd == 0) {
+      a.ws_m[pi] = mn;
+      a.ws_l[pi] = ls;
+    }
+  }
+}
+
+// One workgroup per (sequence, head): merge the splits and write the output.
+template <typename E, int D>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  const int bh = blockIdx.x;
+  const int b = bh / a.H;
+  const int L = a.kv_lens[b];
+  const bool ok = decode_len_ok(L, a.S, a.window, a.is_local);
+  const size_t p0 = (size_t)bh * a.nsplit;
+  float mx = kNegInf;
+  for (int s = 0; s < a.nsplit; ++s)
+    if (a.ws_l[p0 + s] > 0.f) mx = fmaxf(mx, a.ws_m[p0 + s]);
+  float lsum = 0.f;
+  for (int s = 0; s < a.nsplit; ++s) {
+    const float ls = a.ws_l[p0 + s];
+    if (ls > 0.f) lsum += ls * exp2_fast(a.ws_m[p0 + s] - mx);
+  }
+  const float inv = ok ? 1.0f / lsum : __builtin_nanf("");
+  E* orow = static_cast<E*>(a.out) + (size_t)bh * D;
+  for (int dd = threadIdx.x; dd < D; dd += blockDim.x) {
+    float x = 0.f;
+    for (int s = 0; s < a.nsplit; ++s) {
+      const float ls = a.ws_l[p0 + s];
+      if (ls > 0.f) x += a.ws_acc[(p0 + s) * D + dd] * exp2_fast(a.ws_m[p0 + s] - mx);
+    }
+    orow[dd] = (E)(x * inv);
+  }
+}
+
+template <typename E, int D, int G>
+static hipError_t launch_decode_t(DecodeArgs a, int B, int KVH, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_split_kernel<E, D, G>), dim3(a.nsplit, B * KVH), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<E, D>), dim3(B * a.H), dim3(D < 256 ? D : 256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename E>
+static hipError_t launch_decode_e(const DecodeArgs& a, int d, int G, int B, int KVH, hipStream_t stream) {
+  switch (d) {
+    case 64: return G == 2 ? launch_decode_t<E, 64, 2>(a, B, KVH, stream) : launch_decode_t<E, 64, 1>(a, B, KVH, stream);
+    case 128: return G == 2 ? launch_decode_t<E, 128, 2>(a, B, KVH, stream) : launch_decode_t<E, 128, 1>(a, B, KVH, stream);
+    case 256: return G == 2 ? launch_decode_t<E, 256, 2>(a, B, KVH, stream) : launch_decode_t<E, 256, 1>(a, B, KVH, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode(const DecodeLaunch& L, int dtype, hipStream_t stream) {
+  DecodeArgs a;
+  a.q = L.q;
+  a.k = L.k;
+  a.v = L.v;
+  a.out = L.out;
+  a.kv_lens = L.kv_lens;
+  a.B = L.B;
+  a.S = L.S;
+  a.H = L.H;
+  a.KVH = L.KVH;
+  a.cap = make_cap_consts(L.query_scale, L.softcap);
+  a.window = L.window;
+  a.is_local = L.is_local;
+  a.nsplit = decode_splits(L.S);
+  const size_t n = (size_t)L.B * L.H * a.nsplit;
+  float* ws = static_cast<float*>(L.workspace);
+  a.ws_m = ws;
+  a.ws_l = ws + n;
+  a.ws_acc = ws + 2 * n;
+  const int G = L.H / L.KVH;
+  return dtype == 0 ? launch_decode_e<bf16>(a, L.d, G, L.B, L.KVH, stream)
+                    : launch_decode_e<float>(a, L.d, G, L.B, L.KVH, stream);
+}
+
+}  // namespace g2

@@ -1,0 +1,128 @@
+/*
+ * g2attn — Gemma 2 attention layer (prefill and decode) for AMD MI355X (gfx950).
+ *
+ * The operation (Gemma 2 model card on wikillm, "Method" section, one-layer
+ * attention pseudocode; aifetchly "Gemma 2 Guide", section 1 soft-cap formula):
+ *
+ *   for batch b, query row t, query head h, with g = h / (H / KVH) and query
+ *   position p = t + S - T:
+ *     x_j   = query_scale * <q[b,t,h,:], k[b,j,g,:]>
+ *     s_j   = softcap * tanh(x_j / softcap)        (identity if softcap <= 0)
+ *     key j is visible iff j <= p and, on a local layer, j > p - window
+ *     w     = softmax over visible keys of s
+ *     out[b,t,h,:] = sum_j w_j * v[b,j,g,:]
+ *
+ *   The cap acts on the scaled logits before the mask (card, "Paper vs code").
+ *   Every two query heads share one key/value head in all three model sizes
+ *   (card, "Method" item 4 and "Pitfalls", GQA naming); the library accepts
+ *   H / KVH of 1 or 2.  The 27B model's query_scale is 144^-0.5, not
+ *   head_dim^-0.5 (card, "Pitfalls"): the caller passes query_scale, the
+ *   library never derives it.  Local layers use window 4096, global layers see
+ *   the whole causal prefix (card, "Method" item 1).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are device pointers (hipMalloc'd or equivalent) on the current
+ *     device, 16-byte aligned.  The caller owns all buffers; the library never
+ *     allocates device memory and keeps no state between calls.
+ *   - Tensors are dense row-major: q and out (B, T, H, d); k and v (B, S, KVH, d).
+ *   - dtype: G2_BF16 (bf16 storage, fp32 accumulation; bf16 output rounded to
+ *     nearest even) or G2_F32 (fp32 storage and arithmetic).  All tensors of
+ *     one call share the dtype.
+ *   - Calls only enqueue work on `stream` (0 = the null stream) and return; no
+ *     host synchronisation.  `out` must not alias any input.
+ *   - Return value: G2_OK or a negative g2_status; no call aborts or throws.
+ *     Argument errors are detected on the host before anything is enqueued.
+ *
+ * Supported shapes: d in {64, 128, 256}; H / KVH in {1, 2}.
+ */
+#ifndef G2ATTN_H
+#define G2ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { G2_BF16 = 0, G2_F32 = 1 } g2_dtype;
+
+typedef enum {
+  G2_OK = 0,
+  G2_ERR_ARG = -1,         /* null pointer, non-positive size, H % KVH != 0,
+                              T > S, window < 1 on a local layer, T != 1 for
+                              decode, unknown dtype */
+  G2_ERR_UNSUPPORTED = -2, /* d not in {64,128,256} or H/KVH not in {1,2} */
+  G2_ERR_ALIGN = -3,       /* a pointer is not 16-byte aligned */
+  G2_ERR_WORKSPACE = -4,   /* decode workspace missing or too small */
+  G2_ERR_LAUNCH = -5       /* the HIP runtime reported a launch error */
+} g2_status;
+
+/*
+ * Prefill: causal (local: sliding-window) soft-capped GQA attention of T query
+ * rows against S keys/values.
+ *   q, out : (B, T, H, d)       k, v : (B, S, KVH, d)
+ *   query row t sits at position t + S - T (the mask is aligned bottom-right,
+ *   so T = S is ordinary prefill and T < S a chunk continuing a prefix).
+ *   query_scale : multiplies the logits (1/sqrt(d) for 2B/9B, 1/12 for 27B).
+ *   softcap     : cap of cap*tanh(x/cap); <= 0 or +inf disables the cap.
+ *   window      : sliding-window length W of a local layer (key j visible to
+ *                 position p iff p - W < j <= p); ignored when is_local == 0.
+ *   is_local    : 1 for a sliding-window (local) layer, 0 for a global layer.
+ * Work is proportional to the visible (query, key) pairs: tiles wholly outside
+ * the causal / window band are skipped.
+ */
+int g2attn_prefill(const void* q, const void* k, const void* v, void* out,
+                   int B, int T, int S, int H, int KVH, int d,
+                   float query_scale, float softcap, int window, int is_local,
+                   int dtype, hipStream_t stream);
+
+/*
+ * Decode: one new query token per sequence against a KV cache of capacity S
+ * (model card, "Method"; Guide section 2 on local layers keeping only the last
+ * 4096 tokens).
+ *   q, out          : (B, 1, H, d)
+ *   k_cache, v_cache: (B, S, KVH, d); token position j of sequence b lives in
+ *                     slot j mod S, so a local layer's cache of S = window
+ *                     slots is a ring and a global layer's cache is linear.
+ *   kv_lens         : device int32[B]; kv_lens[b] = L_b >= 1 tokens, the
+ *                     newest (already written) at position L_b - 1, which is
+ *                     also the query's position.  Visible positions are those
+ *                     the prefill mask allows; they must fit the cache:
+ *                     L_b <= S for a global layer, min(L_b, window) <= S for a
+ *                     local one.  A sequence whose L_b breaks this rule gets
+ *                     NaN outputs; nothing outside the cache is read.
+ *   T               : must be 1.
+ *   workspace       : device scratch of at least
+ *                     g2attn_decode_workspace_bytes(B, H, d, S) bytes, used for
+ *                     split-K partial results; owned by the caller, may be
+ *                     reused between calls on the same stream.
+ */
+int g2attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                  void* out, const int32_t* kv_lens,
+                  int B, int T, int S, int H, int KVH, int d,
+                  float query_scale, float softcap, int window, int is_local,
+                  int dtype, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream);
+
+/* Bytes of decode workspace needed for these sizes (0 for invalid sizes). */
+size_t g2attn_decode_workspace_bytes(int B, int H, int d, int S);
+
+/*
+ * Host-only validation of the scalar arguments of either entry point
+ * (decode = 1 for decode), returning the status the call would return for
+ * non-null, aligned pointers.  Touches no GPU.
+ */
+int g2attn_check_args(int B, int T, int S, int H, int KVH, int d, int window,
+                      int is_local, int dtype, int decode);
+
+/* Static, human-readable name of a status code. */
+const char* g2attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* G2ATTN_H */

@@ -19,7 +19,7 @@ def _ensure_built():
     if not os.path.exists(oracle_lib):
         from oracle import build as ob
         ob.build()
-    if os.path.exists(os.path.join(ROOT, "attention_g2attn_prefill_amd", "build.py")) and not os.path.exists(hip_lib):
+    if not os.path.exists(hip_lib):
         from attention_g2attn_prefill_amd import build as hb
         hb.build()
 

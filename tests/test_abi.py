@@ -1,0 +1,102 @@
+"""The C-ABI library loads, exports every function include/g2attn.h declares, and
+rejects bad arguments on the host (no GPU is touched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_g2attn_prefill_amd as g2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "g2attn.h")
+
+OK, ARG, UNSUP, ALIGN, WS, LAUNCH = 0, -1, -2, -3, -4, -5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(g2attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("g2attn_prefill", "g2attn_decode", "g2attn_decode_workspace_bytes",
+              "g2attn_check_args", "g2attn_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(g2.library_path)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in (OK, ARG, UNSUP, ALIGN, WS, LAUNCH):
+        assert g2.status_string(code) and g2.status_string(code) != "unknown status"
+    assert g2.status_string(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("args,expect", [
+    # B, T, S, H, KVH, d, window, is_local, dtype, decode
+    ((2, 8192, 8192, 16, 8, 256, 4096, 1, 0, 0), OK),
+    ((1, 256, 256, 4, 2, 64, 64, 0, 1, 0), OK),
+    ((1, 8192, 8192, 32, 16, 128, 4096, 1, 0, 0), OK),
+    ((64, 1, 8192, 16, 8, 256, 4096, 0, 0, 1), OK),
+    ((0, 16, 16, 4, 2, 64, 4, 0, 0, 0), ARG),
+    ((1, 17, 16, 4, 2, 64, 4, 0, 0, 0), ARG),      # T > S
+    ((1, 16, 16, 4, 3, 64, 4, 0, 0, 0), ARG),      # H % KVH
+    ((1, 16, 16, 4, 2, 64, 0, 1, 0, 0), ARG),      # local with window 0
+    ((1, 16, 16, 4, 2, 64, 0, 0, 0, 0), OK),       # window ignored on global
+    ((1, 2, 16, 4, 2, 64, 4, 0, 0, 1), ARG),       # decode with T != 1
+    ((1, 16, 16, 4, 2, 64, 4, 0, 7, 0), ARG),      # unknown dtype
+    ((1, 16, 16, 4, 2, 64, 4, 2, 0, 0), ARG),      # is_local not 0/1
+    ((1, 16, 16, 4, 2, 96, 4, 0, 0, 0), UNSUP),    # d
+    ((1, 16, 16, 8, 2, 64, 4, 0, 0, 0), UNSUP),    # four heads per K/V head
+])
+def test_check_args(args, expect):
+    assert g2.check_args(*args[:8], dtype=args[8], decode=args[9]) == expect
+
+
+def test_workspace_bytes():
+    # splits of 256 positions; per (sequence, head, split): max, sum, d floats
+    assert g2.decode_workspace_bytes(64, 16, 256, 8192) == 64 * 16 * 32 * (2 + 256) * 4
+    assert g2.decode_workspace_bytes(1, 1, 64, 1) == 1 * 1 * 1 * 66 * 4
+    assert g2.decode_workspace_bytes(0, 16, 256, 8192) == 0
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_entry_points_reject_before_launching():
+    lib = g2.lib
+    a = _fake(0x10000)
+    null = ctypes.c_void_p(0)
+    # invalid scalars: rejected before any pointer is looked at
+    assert lib.g2attn_prefill(a, a, a, a, 1, 17, 16, 4, 2, 64, 1.0, 50.0, 4, 0, 0, null) == ARG
+    # null pointer
+    assert lib.g2attn_prefill(null, a, a, a, 1, 16, 16, 4, 2, 64, 1.0, 50.0, 4, 0, 0, null) == ARG
+    # misaligned pointer
+    assert lib.g2attn_prefill(a, _fake(0x10008), a, a, 1, 16, 16, 4, 2, 64, 1.0, 50.0, 4, 0, 0,
+                              null) == ALIGN
+    # decode: missing or short workspace
+    assert lib.g2attn_decode(a, a, a, a, a, 2, 1, 16, 4, 2, 64, 1.0, 50.0, 4, 0, 0, null, 0,
+                             null) == WS
+    need = g2.decode_workspace_bytes(2, 4, 64, 16)
+    assert lib.g2attn_decode(a, a, a, a, a, 2, 1, 16, 4, 2, 64, 1.0, 50.0, 4, 0, 0, a, need - 1,
+                             null) == WS
+    assert lib.g2attn_decode(a, a, a, a, null, 2, 1, 16, 4, 2, 64, 1.0, 50.0, 4, 0, 0, a, need,
+                             null) == ARG
+    assert lib.g2attn_decode(a, a, a, a, a, 2, 1, 16, 4, 2, 64, 1.0, 50.0, 4, 0, 0,
+                             _fake(0x10004), need, null) == ALIGN
+
+
+def test_binding_requires_gpu_tensors():
+    import torch
+    q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        g2.prefill(q, k, k, query_scale=0.125, is_local=False)

@@ -1,0 +1,291 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the CPU fp64 oracle.
+
+Tolerances (stated for the layer's inputs): bf16 storage with fp32
+accumulation, max |diff| <= 2e-2 and mean |diff| <= 2e-3 over the compared
+elements; fp32 storage, max |diff| <= 1e-4.  The oracle consumes exactly the
+values the GPU reads (bf16 values are exact in float32) and returns float64.
+
+Small shapes are compared element by element over the whole output; the
+full-size workloads are compared on sampled rows (first rows, tile and window
+boundaries, the last rows and a seeded random set), with every output also
+checked to be finite.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attention_g2attn_prefill_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX, BF16_MEAN, F32_MAX = 2e-2, 2e-3, 1e-4
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def g2():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import attention_g2attn_prefill_amd as mod
+    return mod
+
+
+def check(got, ref, dtype, what):
+    got = np.asarray(got, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    mx, mean = float(err.max()), float(err.mean())
+    say(f"{what}: max|d|={mx:.3e} mean|d|={mean:.3e}")
+    if dtype == "f32":
+        assert mx <= F32_MAX, f"{what}: max {mx}"
+    else:
+        assert mx <= BF16_MAX, f"{what}: max {mx}"
+        assert mean <= BF16_MEAN, f"{what}: mean {mean}"
+
+
+def layer_kw(cfg, is_local):
+    return dict(query_scale=cfg["query_scale"], softcap=cfg["softcap"], window=cfg["window"],
+                is_local=is_local)
+
+
+# ------------------------------------------------------------ small shapes
+
+SMALL = [
+    # B, T, S, H, KVH, d, window, is_local, dtype, q_mul
+    (1, 256, 256, 4, 2, 64, 64, True, "f32", 4.0),
+    (1, 256, 256, 4, 2, 64, 64, False, "f32", 4.0),
+    (1, 256, 256, 4, 2, 64, 64, True, "f32", 32.0),
+    (2, 300, 300, 4, 2, 256, 64, True, "bf16", 3.0),
+    (2, 300, 300, 4, 2, 256, 64, False, "bf16", 3.0),
+    (1, 300, 300, 4, 2, 128, 37, True, "bf16", 3.0),
+    (1, 300, 300, 4, 2, 64, 100, True, "bf16", 3.0),
+    (2, 300, 300, 4, 4, 128, 50, True, "bf16", 2.0),      # one query head per K/V head
+    (1, 333, 333, 2, 2, 256, 333, False, "bf16", 2.0),
+    (1, 1, 1, 2, 1, 256, 1, True, "bf16", 1.0),            # a single token
+    (1, 17, 17, 2, 1, 128, 4, True, "bf16", 1.0),
+    (1, 200, 200, 2, 1, 256, 1, True, "bf16", 5.0),        # window 1: own value
+    (2, 100, 330, 4, 2, 256, 70, True, "bf16", 3.0),       # T < S: rows at t + S - T
+    (2, 100, 330, 4, 2, 64, 70, False, "bf16", 3.0),
+    (1, 129, 257, 2, 2, 128, 128, False, "f32", 2.0),
+    (1, 250, 250, 4, 2, 256, 64, False, "bf16", 5.5),      # saturating logits
+    (1, 190, 190, 2, 1, 256, 64, True, "f32", 3.0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[
+    f"B{c[0]}T{c[1]}S{c[2]}H{c[3]}K{c[4]}d{c[5]}W{c[6]}{'L' if c[7] else 'G'}-{c[8]}-x{c[9]}"
+    for c in SMALL])
+def test_prefill_small_full(g2, case):
+    B, T, S, H, KVH, d, W, is_local, dt, qm = case
+    say(f"prefill small {case}")
+    seed = 1000 + SMALL.index(case)
+    q = synth.draw((B, T, H, d), seed, 0, dtype=dt, mul=qm)
+    k = synth.draw((B, S, KVH, d), seed, 1, dtype=dt, mul=1.5)
+    v = synth.draw((B, S, KVH, d), seed, 2, dtype=dt)
+    qs = 1.0 / np.sqrt(d)
+    out = g2.prefill(q.cuda(), k.cuda(), v.cuda(), query_scale=qs, softcap=50.0, window=W,
+                     is_local=is_local)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(synth.to_f32_numpy(q), synth.to_f32_numpy(k), synth.to_f32_numpy(v),
+                         query_scale=qs, softcap=50.0, window=W, is_local=is_local)
+    check(synth.to_f32_numpy(out), ref, dt, f"small {case}")
+
+
+def test_prefill_uncapped_and_large_cap(g2):
+    say("prefill cap disabled / huge cap")
+    B, T, H, KVH, d = 1, 160, 4, 2, 128
+    q = synth.draw((B, T, H, d), 7, 0, mul=2.0)
+    k = synth.draw((B, T, KVH, d), 7, 1)
+    v = synth.draw((B, T, KVH, d), 7, 2)
+    qn, kn, vn = (synth.to_f32_numpy(x) for x in (q, k, v))
+    for cap in (0.0, float("inf"), 1e6):
+        out = g2.prefill(q.cuda(), k.cuda(), v.cuda(), query_scale=0.1, softcap=cap, window=40,
+                         is_local=True)
+        torch.cuda.synchronize()
+        ref = oracle.prefill(qn, kn, vn, query_scale=0.1, softcap=cap, window=40, is_local=True)
+        check(synth.to_f32_numpy(out), ref, "bf16", f"cap={cap}")
+
+
+# ------------------------------------------------------- full-size prefill
+
+def sample_rows(B, T, H, W, seed, n_random=160):
+    ts = {0, 1, 2, 15, 16, 31, 32, 63, 64, 65, 127, 128, 255, 256, W - 2, W - 1, W, W + 1,
+          W + 63, W + 64, T // 2, T - 65, T - 64, T - 2, T - 1}
+    ts = sorted(t for t in ts if 0 <= t < T)
+    rows = [((b * T + t) * H + h) for b in range(B) for t in ts for h in range(H)]
+    rng = np.random.default_rng(seed)
+    rows += list(rng.integers(0, B * T * H, size=n_random))
+    return np.unique(np.asarray(rows, np.int64))
+
+
+@pytest.fixture(scope="module")
+def prefill_inputs_cache():
+    return {}
+
+
+@pytest.mark.parametrize("name", ["2b-8k", "9b-8k", "9b-8k-sat", "27b-8k"])
+@pytest.mark.parametrize("is_local", [True, False], ids=["local", "global"])
+def test_prefill_full_size_sampled(g2, name, is_local, prefill_inputs_cache):
+    cfg = synth.WORKLOADS[name]
+    say(f"prefill full {name} {'local' if is_local else 'global'}")
+    if name not in prefill_inputs_cache:
+        prefill_inputs_cache.clear()
+        q, k, v = synth.prefill_inputs(cfg)
+        prefill_inputs_cache[name] = (q, k, v, q.cuda(), k.cuda(), v.cuda(),
+                                      synth.to_f32_numpy(k), synth.to_f32_numpy(v))
+    q, k, v, qd, kd, vd, kn, vn = prefill_inputs_cache[name]
+    kw = layer_kw(cfg, is_local)
+    out = g2.prefill(qd, kd, vd, **kw)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    B, T, H, d = q.shape
+    rows = sample_rows(B, T, H, cfg["window"], seed=cfg["seed"])
+    qn = synth.to_f32_numpy(q)
+    ref = oracle.prefill(qn, kn, vn, rows=rows, **kw)
+    got = synth.to_f32_numpy(out).reshape(-1, d)[rows]
+    check(got, ref, cfg["dtype"], f"{name} {'local' if is_local else 'global'} ({rows.size} rows)")
+
+
+# -------------------------------------------------------------- invariants
+
+def test_window_at_least_T_equals_global_bitwise(g2):
+    say("window >= T: local == global")
+    q = synth.draw((2, 257, 4, 256), 11, 0, mul=3.0).cuda()
+    k = synth.draw((2, 257, 2, 256), 11, 1, mul=3.0).cuda()
+    v = synth.draw((2, 257, 2, 256), 11, 2).cuda()
+    g = g2.prefill(q, k, v, query_scale=1 / 16, softcap=50.0, window=1, is_local=False)
+    for W in (257, 4096):
+        loc = g2.prefill(q, k, v, query_scale=1 / 16, softcap=50.0, window=W, is_local=True)
+        torch.cuda.synchronize()
+        assert torch.equal(loc, g)
+
+
+def test_gqa_equals_repeated_heads(g2):
+    say("GQA == repeated K/V heads (G=1 kernel)")
+    q = synth.draw((1, 300, 4, 128), 12, 0, mul=3.0).cuda()
+    k = synth.draw((1, 300, 2, 128), 12, 1).cuda()
+    v = synth.draw((1, 300, 2, 128), 12, 2).cuda()
+    a = g2.prefill(q, k, v, query_scale=0.09, softcap=50.0, window=64, is_local=True)
+    kr = k.repeat_interleave(2, dim=2).contiguous()
+    vr = v.repeat_interleave(2, dim=2).contiguous()
+    m = g2.prefill(q, kr, vr, query_scale=0.09, softcap=50.0, window=64, is_local=True)
+    torch.cuda.synchronize()
+    d = (a.float() - m.float()).abs()
+    assert float(d.max()) <= 2e-2 and float(d.mean()) <= 2e-3
+
+
+def test_prefill_deterministic_and_canaries(g2):
+    say("determinism + out-of-bounds canaries")
+    B, T, H, KVH, d = 2, 300, 4, 2, 256
+    q = synth.draw((B, T, H, d), 13, 0, mul=3.0).cuda()
+    k = synth.draw((B, T, KVH, d), 13, 1).cuda()
+    v = synth.draw((B, T, KVH, d), 13, 2).cuda()
+    n = B * T * H * d
+    buf = torch.full((n + 4096,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = buf[:n].view(B, T, H, d)
+    g2.prefill(q, k, v, query_scale=1 / 16, softcap=50.0, window=64, is_local=True, out=out)
+    first = out.clone()
+    g2.prefill(q, k, v, query_scale=1 / 16, softcap=50.0, window=64, is_local=True, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(first, out)
+    assert bool(torch.isnan(buf[n:]).all())
+
+
+# ------------------------------------------------------------------ decode
+
+def decode_check(g2, q, kc, vc, lens, cfg_kw, dtype, what, rows=None):
+    out = g2.decode(q.cuda(), kc.cuda(), vc.cuda(), torch.from_numpy(lens).cuda(), **cfg_kw)
+    torch.cuda.synchronize()
+    ref = oracle.decode(synth.to_f32_numpy(q), synth.to_f32_numpy(kc), synth.to_f32_numpy(vc),
+                        lens, **cfg_kw)
+    check(synth.to_f32_numpy(out), ref, dtype, what)
+
+
+@pytest.mark.parametrize("is_local", [True, False], ids=["local", "global"])
+def test_decode_full_size(g2, is_local):
+    cfg = synth.WORKLOADS["9b-decode"]
+    say(f"decode full 9b {'local' if is_local else 'global'}")
+    q, k_g, v_g, lens, k_l, v_l = synth.decode_inputs(cfg, poison=True)
+    kc, vc = (k_l, v_l) if is_local else (k_g, v_g)
+    kw = layer_kw(cfg, is_local)
+    out = g2.decode(q.cuda(), kc.cuda(), vc.cuda(), torch.from_numpy(lens).cuda(), **kw)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    # oracle on a sample of sequences (all heads): slices keep the host copy small
+    bs = [0, 1, int(np.argmin(lens)), int(np.argmax(lens)), 17, 40, 63]
+    bs = sorted(set(bs))
+    ref = oracle.decode(synth.to_f32_numpy(q[bs]), synth.to_f32_numpy(kc[bs]),
+                        synth.to_f32_numpy(vc[bs]), lens[bs], **kw)
+    check(synth.to_f32_numpy(out[bs]), ref, "bf16",
+          f"decode {'local' if is_local else 'global'} seqs {bs}")
+
+
+DECODE_EDGE = [
+    # B, S, H, KVH, d, window, is_local, dtype, lens
+    (5, 4096, 4, 2, 256, 4096, True, "bf16", [1, 100, 4095, 4096, 4097]),
+    (5, 4096, 4, 2, 256, 4096, False, "bf16", [1, 100, 4095, 4096, 2]),
+    (4, 300, 4, 2, 128, 64, True, "bf16", [1, 63, 64, 1000]),
+    (3, 257, 2, 1, 64, 257, True, "bf16", [1, 256, 700]),
+    (3, 600, 4, 4, 128, 50, False, "bf16", [600, 1, 333]),
+    (3, 300, 4, 2, 256, 64, True, "f32", [5, 300, 999]),
+    (2, 300, 4, 2, 64, 64, False, "f32", [300, 7]),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_EDGE, ids=[f"edge{i}" for i in range(len(DECODE_EDGE))])
+def test_decode_edges(g2, case):
+    B, S, H, KVH, d, W, is_local, dt, lens = case
+    say(f"decode edge {case}")
+    lens = np.asarray(lens, np.int32)
+    seed = 300 + len(lens) + d
+    q = synth.draw((B, 1, H, d), seed, 0, dtype=dt, mul=3.0)
+    maxlen = int(lens.max())
+    lin_k = synth.draw((B, max(maxlen, S), KVH, d), seed, 1, dtype=dt)
+    lin_v = synth.draw((B, max(maxlen, S), KVH, d), seed, 2, dtype=dt)
+    if is_local:
+        kc = synth.ring_from_linear(lin_k, lens, S)
+        vc = synth.ring_from_linear(lin_v, lens, S)
+    else:
+        kc, vc = lin_k[:, :S].clone(), lin_v[:, :S].clone()
+        synth.poison_beyond(kc, lens)
+        synth.poison_beyond(vc, lens)
+    kw = dict(query_scale=1 / np.sqrt(d), softcap=50.0, window=W, is_local=is_local)
+    decode_check(g2, q, kc, vc, lens, kw, dt, f"decode edge {case}")
+
+
+def test_decode_invalid_length_gives_nan_only_there(g2):
+    say("decode: a sequence longer than a global cache")
+    q = synth.draw((3, 1, 4, 128), 21, 0)
+    kc = synth.draw((3, 64, 2, 128), 21, 1)
+    vc = synth.draw((3, 64, 2, 128), 21, 2)
+    lens = np.array([64, 65, 10], np.int32)
+    out = g2.decode(q.cuda(), kc.cuda(), vc.cuda(), torch.from_numpy(lens).cuda(),
+                    query_scale=0.1, softcap=50.0, window=64, is_local=False)
+    torch.cuda.synchronize()
+    o = out.float().cpu()
+    assert bool(torch.isnan(o[1]).all())
+    assert bool(torch.isfinite(o[0]).all()) and bool(torch.isfinite(o[2]).all())
+
+
+@pytest.mark.parametrize("is_local", [True, False], ids=["local", "global"])
+def test_decode_equals_last_prefill_row(g2, is_local):
+    say("decode == last prefill row")
+    L, H, KVH, d, W = 777, 4, 2, 256, 100
+    q = synth.draw((1, L, H, d), 31, 0, mul=3.0).cuda()
+    k = synth.draw((1, L, KVH, d), 31, 1).cuda()
+    v = synth.draw((1, L, KVH, d), 31, 2).cuda()
+    pre = g2.prefill(q, k, v, query_scale=1 / 16, softcap=50.0, window=W, is_local=is_local)
+    lens = torch.tensor([L], dtype=torch.int32, device="cuda")
+    dec = g2.decode(q[:, L - 1:L].contiguous(), k, v, lens, query_scale=1 / 16, softcap=50.0,
+                    window=W, is_local=is_local)
+    torch.cuda.synchronize()
+    diff = (pre[:, L - 1].float() - dec[:, 0].float()).abs()
+    assert float(diff.max()) <= 2e-2
