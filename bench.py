@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gemma 2 attention layer on one MI355X.
+
+One step = the whole hot path on seeded synthetic inputs shaped like Gemma 2 9B:
+  prefill of a local (sliding window 4096) and a global layer at B=2, T=S=8192,
+  H=16, KVH=8, d=256, softcap 50, query_scale 1/16; then decode of one token
+  for 64 sequences against a global linear cache (L_b uniform on [4096, 8192])
+  and a local 4096-slot ring.
+
+Reported (one JSON line):
+  value    prefill effective TFLOP/s = algorithmic FLOPs of the pair / prefill
+           kernel time, counting 4*d FLOPs per visible (query head, key) pair
+           only (QK^T and PV, 2*d each); masked pairs are not counted;
+  decode   KV GB/s = visible K/V bytes (plus q and out) / decode time;
+  roofline the prefill kernel against the bf16 dense MFMA peak (2.5 PFLOP/s),
+           durations from HIP events on the launch stream over the timed steps;
+  cpu_baseline the fp64 oracle on a bounded sample of the same workload.
+"""
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = ("prefill eff. TFLOP/s (% bf16 MFMA peak) @9B 8K; "
+          "decode KV GB/s (% HBM peak)")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_9b_8k_traffic.txt")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-rows", type=int, default=40960,
+                    help="rows per layer of the oracle's bounded CPU sample (0: none)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed steps, run one device copy of this many MiB "
+                         "(reference kernel for HBM counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "attention_g2attn_prefill_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def prefill_pairs(T, S, window, is_local):
+    """Visible (query, key) pairs of one (batch, head) slice."""
+    tot = 0
+    off = S - T
+    for t in range(T):
+        p = t + off
+        lo = max(0, p - window + 1) if is_local else 0
+        tot += p - lo + 1
+    return tot
+
+
+def measured_traffic(src_hash):
+    """HBM bytes per prefill launch from committed counter runs, if they were
+    taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.loads(fh.read())
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != src_hash:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(cfg, q, k, v, rows_per_layer):
+    import numpy as np
+    import oracle
+    from attention_g2attn_prefill_amd import synth
+
+    B, T, H, d = q.shape
+    S = k.shape[1]
+    qn, kn, vn = (synth.to_f32_numpy(x) for x in (q, k, v))
+    rng = np.random.default_rng(0)
+    flops, secs = 0.0, 0.0
+    for is_local in (True, False):
+        rows = rng.integers(0, B * T * H, size=rows_per_layer)
+        t = (rows // H) % T
+        p = t + (S - T)
+        lo = np.maximum(0, p - cfg["window"] + 1) if is_local else np.zeros_like(p)
+        flops += float(4 * d * (p - lo + 1).sum())
+        t0 = time.perf_counter()
+        oracle.prefill(qn, kn, vn, rows=rows, query_scale=cfg["query_scale"],
+                       softcap=cfg["softcap"], window=cfg["window"], is_local=is_local)
+        secs += time.perf_counter() - t0
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": (f"{rows_per_layer} seeded random (b,t,h) rows of each layer of the "
+                       f"9B 8K local+global pair, every visible key; {secs:.1f} s, "
+                       f"{flops / 1e9:.0f} GFLOP counted like the GPU")}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build "
+              "measures the single-GPU kernels and has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1:
+        sys.exit("--steps must be >= 1")
+
+    import numpy as np
+    import torch
+    import attention_g2attn_prefill_amd as g2
+    from attention_g2attn_prefill_amd import synth
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    cfg_p = synth.WORKLOADS["9b-8k"]
+    cfg_d = synth.WORKLOADS["9b-decode"]
+
+    # ---- inputs, resident in HBM before timing
+    q, k, v = synth.prefill_inputs(cfg_p)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out_l = torch.empty_like(qd)
+    out_g = torch.empty_like(qd)
+    dq, k_g, v_g, lens, k_l, v_l = synth.decode_inputs(cfg_d)
+    dqd = dq.to(dev)
+    kgd, vgd, kld, vld = (x.to(dev) for x in (k_g, v_g, k_l, v_l))
+    del k_g, v_g, k_l, v_l
+    lens_d = torch.from_numpy(lens).to(dev)
+    dout_l = torch.empty_like(dqd)
+    dout_g = torch.empty_like(dqd)
+    B, T, H, d = q.shape
+    S, KVH = k.shape[1], k.shape[2]
+    DB, DS, DH, DKVH, Dd = dq.shape[0], kgd.shape[1], dq.shape[2], kgd.shape[2], dq.shape[3]
+    W = cfg_p["window"]
+    ws = torch.empty(g2.decode_workspace_bytes(DB, DH, Dd, DS), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    kw_p = dict(query_scale=cfg_p["query_scale"], softcap=cfg_p["softcap"], window=W)
+    kw_d = dict(query_scale=cfg_d["query_scale"], softcap=cfg_d["softcap"],
+                window=cfg_d["window"])
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        g2.prefill(qd, kd, vd, is_local=True, out=out_l, stream=stream, **kw_p)
+        if ev is not None:
+            ev[1].record(stream)
+        g2.prefill(qd, kd, vd, is_local=False, out=out_g, stream=stream, **kw_p)
+        if ev is not None:
+            ev[2].record(stream)
+        g2.decode(dqd, kld, vld, lens_d, is_local=True, out=dout_l, workspace=ws,
+                  stream=stream, **kw_d)
+        if ev is not None:
+            ev[3].record(stream)
+        g2.decode(dqd, kgd, vgd, lens_d, is_local=False, out=dout_g, workspace=ws,
+                  stream=stream, **kw_d)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"[bench] timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    ms = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(4)]
+                   for i in range(args.steps)])  # per step: pl, pg, dl, dg (ms)
+    t_pl, t_pg, t_dl, t_dg = ms.mean(axis=0) * 1e-3
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---- algorithmic work
+    f_local = 4.0 * d * B * H * prefill_pairs(T, S, W, True)
+    f_global = 4.0 * d * B * H * prefill_pairs(T, S, W, False)
+    prefill_tflops = (f_local + f_global) / (t_pl + t_pg) / 1e12
+    row_bytes = 2 * DKVH * Dd * 2  # K and V bytes per visible position (bf16)
+    n_local = np.minimum(lens.astype(np.int64), cfg_d["window"]).sum()
+    n_global = lens.astype(np.int64).sum()
+    qo_bytes = 2 * DB * DH * Dd * 2
+    b_local = float(n_local * row_bytes + qo_bytes)
+    b_global = float(n_global * row_bytes + qo_bytes)
+    decode_gbs = (b_local + b_global) / (t_dl + t_dg) / 1e9
+
+    src_hash = kernel_source_hash()
+    traffic = measured_traffic(src_hash)
+    roofline = {"bound": "mfma", "achieved": round(prefill_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(prefill_tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic}
+    decode = {"metric": "decode KV GB/s", "value": round(decode_gbs, 1), "unit": "GB/s",
+              "frac_of_hbm_peak": round(decode_gbs / PEAK_HBM_GBS, 4),
+              "roofline": {"bound": "hbm", "achieved": round(decode_gbs, 1),
+                           "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": round(decode_gbs / PEAK_HBM_GBS, 4), "traffic": None},
+              "ms_local": round(t_dl * 1e3, 4), "ms_global": round(t_dg * 1e3, 4),
+              "bytes_local": b_local, "bytes_global": b_global}
+    per_layer = {"prefill_local_ms": round(t_pl * 1e3, 4), "prefill_global_ms": round(t_pg * 1e3, 4),
+                 "prefill_local_tflops": round(f_local / t_pl / 1e12, 2),
+                 "prefill_global_tflops": round(f_global / t_pg / 1e12, 2),
+                 "prefill_flops_local": f_local, "prefill_flops_global": f_global}
+
+    cpu = None
+    if args.cpu_rows > 0:
+        cpu = cpu_baseline(cfg_p, q, k, v, args.cpu_rows)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(prefill_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes of the Gemma 2 9B attention layer)",
+        "config": {"workload": "gemma2-9b attention: prefill local+global pair B=2 T=S=8192 "
+                               "H=16 KVH=8 d=256 W=4096 cap=50; decode B=64 global "
+                               "L~U[4096,8192] + local ring 4096",
+                   "global_batch": B, "seq_len": T, "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "decode": decode,
+        "per_layer": per_layer,
+        "kernel_source_sha256": src_hash[:16],
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

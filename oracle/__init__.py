@@ -50,6 +50,8 @@ def _load():
     lib.g2o_decode.argtypes = [_f32p, _f32p, _f32p, _i32p, _f64p, _I, _I, _I,
                                _I, _I, _D, _D, _I, _I, _i64p, ctypes.c_int64]
     lib.g2o_decode.restype = _I
+    lib.g2o_threads.argtypes = []
+    lib.g2o_threads.restype = _I
     _lib = lib
     return lib
 
@@ -76,6 +78,11 @@ def softcap(x, cap):
     """cap * tanh(x / cap) in double; identity when cap <= 0 or cap = inf."""
     lib = _load()
     return lib.g2o_softcap(float(x), float(cap))
+
+
+def threads():
+    """Threads the oracle's parallel loops use."""
+    return int(_load().g2o_threads())
 
 
 def allowed(p, j, window, is_local):

@@ -271,3 +271,15 @@ int g2o_decode(const float* q, const float* k_cache, const float* v_cache,
   }
   return G2O_OK;
 }
+
+/* Number of threads the parallel loops above use (OpenMP's default team). */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+int g2o_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
