@@ -10,26 +10,40 @@
 //  * One workgroup = 4 waves = 128 query rows that all read the same K/V head:
 //    with two query heads per K/V head (the card's "Method" item 4) that is 64
 //    positions x 2 heads, so every K/V tile staged in LDS serves both heads.
+//  * K and V tiles go from global memory straight into LDS with
+//    global_load_lds_dwordx4 (no staging registers), double-buffered: the
+//    loads of tile i+1 are in flight while tile i is computed, and one
+//    barrier per tile both publishes tile i+1 and retires tile i.  A tile is
+//    stored as groups of four 16-byte chunks: byte (c/4)*BN*64 + r*64 +
+//    16*((c%4) ^ sw(r)) holds chunk c of row r, so each wave-wide 1 KiB copy
+//    fills 16 rows x 64 bytes, the XOR keeps the operand reads below on
+//    distinct LDS banks, and all per-lane address terms are loop-invariant.
 //  * Transposed scores: each wave computes S^T = K * Q^T (keys x queries) with
 //    K from LDS as the A operand and its 32 queries' Q^T kept in registers as
-//    the B operand.  The accumulator layout then gives every lane whole
-//    columns (queries), so the softmax row statistics are per-lane values and
-//    P^T feeds the P*V product (O^T = V^T * P^T) straight from registers.
-//  * V is transposed once on its way into LDS (4 keys x 8 dims per thread,
-//    repacked in registers), so V^T operands are plain 8-byte LDS reads.
-//  * Soft-cap, mask and online softmax run in fp32 in base 2 (log2(e) is folded
-//    into the constants).  The running max is rescaled lazily: only when a
-//    row's max grows by more than 8 (log2 units) are O and l multiplied down.
+//    the B operand.  Every lane then owns whole query columns, so softmax row
+//    statistics are per-lane values, and P^T feeds O^T = V^T * P^T straight
+//    from registers.  The V^T operand comes from the row-major V tile through
+//    the LDS transpose read (ds_read_b64_tr_b16): within each 16-lane group,
+//    lane 4a+c receives element c of the rows read by lanes a, a+4, a+8, a+12.
+//  * Soft-cap, mask and online softmax run in fp32 in base 2.  With the fast
+//    cap form s = C - 2C*r, r = 1/(1+e^{2y}), the row max is taken on r (a
+//    min) and p = 2^(fma(r, -2C, C - m)), one VALU op less per logit.  The
+//    running max is rescaled lazily: O and l are multiplied down only when a
+//    row's max grows by more than 8 (log2 units).
 //  * Tiles wholly outside the causal / sliding-window band are skipped; the
 //    mask is evaluated only on tiles that cross the band's edges.
-//  * Work order: heaviest query blocks first (causal rows near the end see the
-//    most keys); consecutive workgroups take different (batch, kv-head) pairs,
-//    which the dispatcher spreads over the 8 XCDs, so each XCD's L2 keeps
-//    serving the same K/V heads.
+//  * Work order: heaviest query blocks first; consecutive workgroups take
+//    different (batch, kv-head) pairs, which the dispatcher spreads over the 8
+//    XCDs, so each XCD's L2 keeps serving the same K/V heads.
 #include "g2_device.h"
 #include "g2_kernels.h"
 
 namespace g2 {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+#define G2_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define G2_LDS_S16X4(p) ((__attribute__((address_space(3))) s16x4*)(p))
 
 template <int D, int G, int BN>
 struct PrefillShape {
@@ -42,12 +56,20 @@ struct PrefillShape {
   static constexpr int kDB = D / 16;              // 16-row blocks of O^T
   static constexpr int kNB = BN / 16;             // 16-key blocks per tile
   static constexpr int kKS = BN / 32;             // 32-key steps of P*V
-  static constexpr int kKStr = D + 8;             // K row stride in LDS (elements)
-  static constexpr int kVStr = BN + 4;            // V^T row stride in LDS (elements)
-  static constexpr int kLdsBytes = (BN * kKStr + D * kVStr) * 2;
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kCPR = D / 8;              // 16-byte chunks per row
+  static constexpr int kTileBytes = BN * kRowBytes;
+  static constexpr int kDmaPerTile = kTileBytes / 1024;   // wave-wide 1 KiB copies
+  static constexpr int kDmaPerWave = kDmaPerTile / kWaves;
+  static constexpr int kRowGroups = BN / 16;                // 16-row groups per tile
   static_assert(BN % 32 == 0, "tile must hold whole 32-key steps");
   static_assert(G == 1 || G == 2, "one or two query heads per K/V head");
+  static_assert(kDmaPerTile % kWaves == 0, "tile copies split evenly over waves");
 };
+
+// Chunk-in-group swizzles of the K and V tiles (see the layout above).
+__device__ __forceinline__ int swz_k(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int swz_v(int r) { return ((r >> 2) & 1) << 1; }
 
 struct PrefillArgs {
   const bf16* q;
@@ -61,12 +83,12 @@ struct PrefillArgs {
   int n_mblocks;
 };
 
-template <int D, int G, int BN>
+template <int D, int G, int BN, int CAP>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   using P = PrefillShape<D, G, BN>;
   constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
-  __shared__ __attribute__((aligned(16))) bf16 k_lds[BN * P::kKStr];
-  __shared__ __attribute__((aligned(16))) bf16 vt_lds[D * P::kVStr];
+  // [buffer][K|V] tiles, each BN rows of D bf16, rows stored whole and swizzled
+  __shared__ __attribute__((aligned(1024))) char lds[2][2][P::kTileBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -104,14 +126,53 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   const int wg_p_first = mb * P::kBMP + off;
   const int wg_p_last = wg_t_last + off;
   const int j_lo = a.is_local ? max(0, wg_p_first - a.window + 1) : 0;
-  const int j_hi = wg_p_last;  // inclusive, <= S-1
   const int n_start = (j_lo / BN) * BN;
+  const int n_tiles = (wg_p_last - n_start) / BN + 1;
 
   const bool wave_active = t0 < T;
   const int w_p_first = t0 + off;
   const int w_p_last = min(t0 + P::kQPW - 1, T - 1) + off;
   const int w_j_lo = a.is_local ? max(0, w_p_first - a.window + 1) : 0;
   const int w_j_lo_last = a.is_local ? max(0, w_p_last - a.window + 1) : 0;
+
+  // ---- tile copies.  Copy n fills 16 rows (16*(n % kRowGroups) + lane/4)
+  // with chunk group n / kRowGroups; lane i writes physical chunk i%4, which
+  // holds logical chunk (i%4) ^ swz(row).  Every per-lane term is the same for
+  // all copies of all tiles; only the row-group / chunk-group part varies.
+  const size_t kv_row_stride = (size_t)KVH * D;
+  const unsigned row_bytes = (unsigned)kv_row_stride * 2u;
+  const char* kbase = reinterpret_cast<const char*>(a.k + ((size_t)b * S * KVH + g) * D);
+  const char* vbase = reinterpret_cast<const char*>(a.v + ((size_t)b * S * KVH + g) * D);
+  const unsigned dma_rl = lane >> 2;  // row within the 16-row group
+  const unsigned dma_kchunk = (lane & 3) ^ swz_k(dma_rl);
+  const unsigned dma_vchunk = (lane & 3) ^ swz_v(dma_rl);
+  const unsigned dma_klane = dma_rl * row_bytes + dma_kchunk * 16u;
+  const unsigned dma_vlane = dma_rl * row_bytes + dma_vchunk * 16u;
+  // Copies of tile n0 into `dst` (K then V halves of one buffer).  In a last,
+  // partial tile, lanes whose row lies past S copy nothing; those LDS rows
+  // keep earlier finite data (the buffers start zeroed) and are masked.
+  auto issue_tile = [&](char (*__restrict__ dst)[P::kTileBytes], int n0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < P::kDmaPerWave; ++c) {
+      const int n = wave + c * P::kWaves;
+      const int cg = n / P::kRowGroups, r0 = 16 * (n % P::kRowGroups);
+      const size_t uni = (size_t)(n0 + r0) * row_bytes + 64u * cg;  // wave-uniform
+      if (n0 + r0 + (int)dma_rl < S) {
+        __builtin_amdgcn_global_load_lds(kbase + uni + dma_klane, G2_LDS(&dst[0][n * 1024]), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vbase + uni + dma_vlane, G2_LDS(&dst[1][n * 1024]), 16, 0, 0);
+      }
+    }
+  };
+
+  // ---- per-lane LDS read offsets (bytes within a tile)
+  // K operand (row kb*16 + l16, chunk 4*kk + lq):
+  //   kk*BN*64 + kb*1024 + l16*64 + 16*(lq ^ swz_k(l16))
+  const int k_lane = l16 * 64 + ((lq ^ swz_k(l16)) << 4);
+  // V transpose read (row 32*ks + 16*half + 4*lq + l16/4, dims 16*db + 4*(l16%4)):
+  //   (db/2)*BN*64 + (32*ks + 16*half)*64 + v_lane[db % 2]
+  const int v_common = (4 * lq + (l16 >> 2)) * 64 + (((l16 & 3) >> 1) << 4) + 8 * (l16 & 1);
+  const int v_lane0 = v_common + 32 * (lq & 1);
+  const int v_lane1 = v_common + 32 * ((lq & 1) ^ 1);
 
   f32x4 o[P::kDB][2];
 #pragma unroll
@@ -120,73 +181,16 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
     for (int qb = 0; qb < 2; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {kNegInf, kNegInf};
   float l_run[2] = {0.f, 0.f};
+  const float k_in = a.cap.k_in, c_out = a.cap.c_out;
 
-  const size_t kv_row_stride = (size_t)KVH * D;
-  const bf16* kbase = a.k + ((size_t)b * S * KVH + g) * D;
-  const bf16* vbase = a.v + ((size_t)b * S * KVH + g) * D;
-
-  for (int n0 = n_start; n0 <= j_hi; n0 += BN) {
-    // ---- stage K (row-major) and V^T (dim-major) tiles in LDS
-    constexpr int kKCh = D / 8;           // 16-byte chunks per K row
-    constexpr int kKU = BN * kKCh;        // K chunks per tile
-    constexpr int kNKG = BN / 4;          // 4-key groups
-    constexpr int kVU = kNKG * (D / 8);   // V transpose units (4 keys x 8 dims)
-    constexpr int kKIt = (kKU + P::kThreads - 1) / P::kThreads;
-    constexpr int kVIt = (kVU + P::kThreads - 1) / P::kThreads;
-    __syncthreads();  // previous tile fully consumed
-    {
-      u32x4 kreg[kKIt];
-#pragma unroll
-      for (int it = 0; it < kKIt; ++it) {
-        const int u = tid + it * P::kThreads;
-        const int row = u / kKCh, c = u % kKCh;
-        const int j = n0 + row;
-        kreg[it] = u32x4{0u, 0u, 0u, 0u};
-        if (u < kKU && j < S) kreg[it] = *reinterpret_cast<const u32x4*>(kbase + j * kv_row_stride + c * 8);
-      }
-#pragma unroll
-      for (int it = 0; it < kKIt; ++it) {
-        const int u = tid + it * P::kThreads;
-        const int row = u / kKCh, c = u % kKCh;
-        if (u < kKU) *reinterpret_cast<u32x4*>(&k_lds[row * P::kKStr + c * 8]) = kreg[it];
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < kVIt; ++it) {
-      const int u = tid + it * P::kThreads;
-      const int kg = u % kNKG, dg = u / kNKG;
-      u32x4 vreg[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = n0 + kg * 4 + r;
-        vreg[r] = u32x4{0u, 0u, 0u, 0u};
-        if (u < kVU && j < S) vreg[r] = *reinterpret_cast<const u32x4*>(vbase + j * kv_row_stride + dg * 8);
-      }
-      if (u < kVU) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // dword e of each key row holds dims (8dg+2e, 8dg+2e+1)
-          const uint32_t r0 = vreg[0][e], r1 = vreg[1][e];
-          const uint32_t r2 = vreg[2][e], r3 = vreg[3][e];
-          u32x2 lo, hi;
-          lo[0] = (r0 & 0xffffu) | (r1 << 16);
-          lo[1] = (r2 & 0xffffu) | (r3 << 16);
-          hi[0] = (r0 >> 16) | (r1 & 0xffff0000u);
-          hi[1] = (r2 >> 16) | (r3 & 0xffff0000u);
-          const int d0 = dg * 8 + 2 * e;
-          *reinterpret_cast<u32x2*>(&vt_lds[d0 * P::kVStr + kg * 4]) = lo;
-          *reinterpret_cast<u32x2*>(&vt_lds[(d0 + 1) * P::kVStr + kg * 4]) = hi;
-        }
-      }
-    }
-    __syncthreads();
-
-    // ---- does this wave see any key of the tile?
-    if (!wave_active || n0 > w_p_last || n0 + BN - 1 < w_j_lo) continue;
+  auto compute_tile = [&](const char (*__restrict__ buf)[P::kTileBytes], int n0) __attribute__((always_inline)) {
+    if (!wave_active || n0 > w_p_last || n0 + BN - 1 < w_j_lo) return;
     const bool need_mask = (n0 + BN - 1 > w_p_first) || (n0 + BN > S) ||
                            (a.is_local && n0 < w_j_lo_last);
+    const char* kt = buf[0];
+    const char* vt = buf[1];
 
-    // ---- S^T = K * Q^T
+    // ---- S^T = K * Q^T; K operand: row kb*16 + l16, logical chunk 4*kk + lq
     f32x4 st[P::kNB][2];
 #pragma unroll
     for (int kb = 0; kb < P::kNB; ++kb)
@@ -196,51 +200,60 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
     for (int kk = 0; kk < P::kKK; ++kk) {
 #pragma unroll
       for (int kb = 0; kb < P::kNB; ++kb) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&k_lds[(kb * 16 + l16) * P::kKStr + kk * 32 + lq * 8]);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + kk * (BN * 64) + kb * 1024 + k_lane);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           st[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][kk], st[kb][qb], 0, 0, 0);
       }
     }
 
-    // ---- soft-cap (log2 units) and mask; the cap form is uniform per launch
-    auto cap_and_mask = [&](auto capfn) {
+    // ---- soft-cap + mask.  Fast form keeps r = 1/(1+e^{2y}) (s = C - 2C r,
+    // decreasing in r; masked: r = +inf); other forms keep s (masked: -inf).
 #pragma unroll
-      for (int kb = 0; kb < P::kNB; ++kb) {
+    for (int kb = 0; kb < P::kNB; ++kb) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float s2 = capfn(st[kb][qb][i]);
-            if (need_mask) {
-              const int j = n0 + kb * 16 + lq * 4 + i;
-              const int p = t0 + qb * 16 + l16 + off;
-              const bool vis = (j <= p) && (j < S) && (!a.is_local || j > p - a.window);
-              s2 = vis ? s2 : kNegInf;
-            }
-            st[kb][qb][i] = s2;
+        for (int i = 0; i < 4; ++i) {
+          const float x = st[kb][qb][i];
+          float z;
+          if constexpr (CAP == kCapFast) z = rcp_fast(1.0f + exp2_fast(x * k_in));
+          else if constexpr (CAP == kCapAccurate) z = capped_log2_accurate(x, k_in, c_out);
+          else z = x * k_in;
+          if (need_mask) {
+            const int j = n0 + kb * 16 + lq * 4 + i;
+            const int p = t0 + qb * 16 + l16 + off;
+            const bool vis = (j <= p) && (j < S) && (!a.is_local || j > p - a.window);
+            if constexpr (CAP == kCapFast) z = vis ? z : __builtin_inff();
+            else z = vis ? z : kNegInf;
           }
+          st[kb][qb][i] = z;
         }
       }
-    };
-    const float k_in = a.cap.k_in, c_out = a.cap.c_out;
-    if (a.cap.mode == kCapFast)
-      cap_and_mask([&](float x) { return capped_log2_fast(x, k_in, c_out); });
-    else if (a.cap.mode == kCapAccurate)
-      cap_and_mask([&](float x) { return capped_log2_accurate(x, k_in, c_out); });
-    else
-      cap_and_mask([&](float x) { return x * k_in; });
+    }
 
     // ---- online softmax (per lane: two query columns)
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float mt = kNegInf;
+      float mt;
+      if constexpr (CAP == kCapFast) {
+        float rmin = __builtin_inff();
 #pragma unroll
-      for (int kb = 0; kb < P::kNB; ++kb)
+        for (int kb = 0; kb < P::kNB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mt = fmaxf(mt, st[kb][qb][i]);
-      mt = fmaxf(mt, shfl_xor(mt, 16));
-      mt = fmaxf(mt, shfl_xor(mt, 32));
+          for (int i = 0; i < 4; ++i) rmin = fminf(rmin, st[kb][qb][i]);
+        rmin = fminf(rmin, shfl_xor(rmin, 16));
+        rmin = fminf(rmin, shfl_xor(rmin, 32));
+        mt = __builtin_fmaf(-2.0f * c_out, rmin, c_out);  // -inf when all masked
+      } else {
+        mt = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < P::kNB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mt = fmaxf(mt, st[kb][qb][i]);
+        mt = fmaxf(mt, shfl_xor(mt, 16));
+        mt = fmaxf(mt, shfl_xor(mt, 32));
+      }
       const bool grow = mt > m_run[qb] + kTau;  // true also for the first visible keys
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {
         const float m_new = grow ? mt : m_run[qb];
@@ -252,18 +265,32 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
       }
       const float m_use = (m_run[qb] == kNegInf) ? 0.0f : m_run[qb];
       float ls = 0.f;
+      if constexpr (CAP == kCapFast) {
+        const float base = c_out - m_use;
+        const float slope = -2.0f * c_out;
 #pragma unroll
-      for (int kb = 0; kb < P::kNB; ++kb)
+        for (int kb = 0; kb < P::kNB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = exp2_fast(st[kb][qb][i] - m_use);
-          st[kb][qb][i] = p;
-          ls += p;
-        }
+          for (int i = 0; i < 4; ++i) {
+            const float p = exp2_fast(__builtin_fmaf(st[kb][qb][i], slope, base));
+            st[kb][qb][i] = p;
+            ls += p;
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < P::kNB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = exp2_fast(st[kb][qb][i] - m_use);
+            st[kb][qb][i] = p;
+            ls += p;
+          }
+      }
       l_run[qb] += ls;
     }
 
-    // ---- O^T += V^T * P^T
+    // ---- O^T += V^T * P^T; V^T operand rows (keys) 32*ks + 4*lq + j and
+    // 32*ks + 16 + 4*lq + j, column (dim) 16*db + l16, via transpose reads
 #pragma unroll
     for (int ks = 0; ks < P::kKS; ++ks) {
       bf16x8 pf[2];
@@ -278,15 +305,45 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
       }
 #pragma unroll
       for (int db = 0; db < P::kDB; ++db) {
-        const bf16* vrow = &vt_lds[(db * 16 + l16) * P::kVStr + ks * 32 + lq * 4];
-        const u32x2 a0 = *reinterpret_cast<const u32x2*>(vrow);
-        const u32x2 a1 = *reinterpret_cast<const u32x2*>(vrow + 16);
-        const u32x4 aw = {a0[0], a0[1], a1[0], a1[1]};
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, aw);
+        const char* vb = vt + (db >> 1) * (BN * 64) + (32 * ks) * 64 + ((db & 1) ? v_lane1 : v_lane0);
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G2_LDS_S16X4(vb));
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G2_LDS_S16X4(vb + 16 * 64));
+        const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, vv);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb], o[db][qb], 0, 0, 0);
       }
+    }
+  };
+
+  // ---- pipeline: tile i+1 is copied into the other buffer while tile i is
+  // computed; one barrier per tile.  The copy and the compute of one step
+  // see their two buffers through restrict pointers, so the compiler knows
+  // the copies in flight never overlap the LDS being read and does not wait
+  // for them before the operand reads.
+  auto step = [&](const char (*__restrict__ cur)[P::kTileBytes],
+                  char (*__restrict__ nxt)[P::kTileBytes], int n0, bool prefetch) __attribute__((always_inline)) {
+    if (prefetch) issue_tile(nxt, n0 + BN);
+    compute_tile(cur, n0);
+  };
+  {
+    u32x4* z = reinterpret_cast<u32x4*>(&lds[0][0][0]);
+    for (int i = tid; i < (int)(sizeof(lds) / 16); i += P::kThreads) z[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  issue_tile(lds[0], n_start);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int it = 0; it < n_tiles; it += 2) {
+    const int n0 = n_start + it * BN;
+    step(lds[0], lds[1], n0, it + 1 < n_tiles);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (it + 1 < n_tiles) {
+      step(lds[1], lds[0], n0 + BN, it + 2 < n_tiles);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
     }
   }
 
@@ -312,9 +369,26 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   }
 }
 
-template <int D, int G, int BN>
-static hipError_t launch_prefill_bf16_t(const PrefillLaunch& L, hipStream_t stream) {
+template <int D, int G, int BN, int CAP>
+static hipError_t launch_prefill_bf16_t(const PrefillArgs& a, int B, hipStream_t stream) {
   using P = PrefillShape<D, G, BN>;
+  const unsigned grid = (unsigned)a.n_mblocks * (unsigned)(B * a.KVH);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, G, BN, CAP>), dim3(grid), dim3(P::kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, int G, int BN>
+static hipError_t launch_prefill_bf16_dg(PrefillArgs a, const PrefillLaunch& L, hipStream_t stream) {
+  using P = PrefillShape<D, G, BN>;
+  a.n_mblocks = (L.T + P::kBMP - 1) / P::kBMP;
+  switch (a.cap.mode) {
+    case kCapFast: return launch_prefill_bf16_t<D, G, BN, kCapFast>(a, L.B, stream);
+    case kCapAccurate: return launch_prefill_bf16_t<D, G, BN, kCapAccurate>(a, L.B, stream);
+    default: return launch_prefill_bf16_t<D, G, BN, kCapNone>(a, L.B, stream);
+  }
+}
+
+hipError_t launch_prefill_bf16(const PrefillLaunch& L, hipStream_t stream) {
   PrefillArgs a;
   a.q = static_cast<const bf16*>(L.q);
   a.k = static_cast<const bf16*>(L.k);
@@ -327,21 +401,15 @@ static hipError_t launch_prefill_bf16_t(const PrefillLaunch& L, hipStream_t stre
   a.cap = make_cap_consts(L.query_scale, L.softcap);
   a.window = L.window;
   a.is_local = L.is_local;
-  a.n_mblocks = (L.T + P::kBMP - 1) / P::kBMP;
-  const unsigned grid = (unsigned)a.n_mblocks * (unsigned)(L.B * L.KVH);
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, G, BN>), dim3(grid), dim3(P::kThreads), 0, stream, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_prefill_bf16(const PrefillLaunch& L, hipStream_t stream) {
+  a.n_mblocks = 0;
   const int G = L.H / L.KVH;
   switch (L.d) {
     case 64:
-      return G == 2 ? launch_prefill_bf16_t<64, 2, 64>(L, stream) : launch_prefill_bf16_t<64, 1, 64>(L, stream);
+      return G == 2 ? launch_prefill_bf16_dg<64, 2, 64>(a, L, stream) : launch_prefill_bf16_dg<64, 1, 64>(a, L, stream);
     case 128:
-      return G == 2 ? launch_prefill_bf16_t<128, 2, 64>(L, stream) : launch_prefill_bf16_t<128, 1, 64>(L, stream);
+      return G == 2 ? launch_prefill_bf16_dg<128, 2, 64>(a, L, stream) : launch_prefill_bf16_dg<128, 1, 64>(a, L, stream);
     case 256:
-      return G == 2 ? launch_prefill_bf16_t<256, 2, 32>(L, stream) : launch_prefill_bf16_t<256, 1, 32>(L, stream);
+      return G == 2 ? launch_prefill_bf16_dg<256, 2, 32>(a, L, stream) : launch_prefill_bf16_dg<256, 1, 32>(a, L, stream);
     default:
       return hipErrorInvalidValue;
   }
