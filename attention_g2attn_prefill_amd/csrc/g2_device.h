@@ -99,6 +99,36 @@ __device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) {
   return __builtin_bit_cast(float, w & 0xffff0000u);
 }
 
+// All-reduce over the lane pairs (l, l^16) and (l, l^32) of a wave64 using the
+// gfx950 row / half-wave swaps (plain VALU, no LDS round trip).  After
+// v_permlane16_swap(x, x) the two results hold, in every lane, x of the lane
+// itself and of lane l^16 (in some order); likewise v_permlane32_swap for
+// l^32.  Applying a commutative op to the pair therefore reduces over both.
+// The second operand goes through an empty asm so the compiler cannot treat
+// the two inputs as one value (it would then fold the pair to one result).
+__device__ __forceinline__ unsigned opaque_copy(unsigned x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+template <typename Op>
+__device__ __forceinline__ float reduce_xor16_32(float v, Op op) {
+  unsigned u = __builtin_bit_cast(unsigned, v);
+  auto a = __builtin_amdgcn_permlane16_swap(u, opaque_copy(u), false, false);
+  v = op(__builtin_bit_cast(float, (unsigned)a[0]), __builtin_bit_cast(float, (unsigned)a[1]));
+  u = __builtin_bit_cast(unsigned, v);
+  auto b = __builtin_amdgcn_permlane32_swap(u, opaque_copy(u), false, false);
+  return op(__builtin_bit_cast(float, (unsigned)b[0]), __builtin_bit_cast(float, (unsigned)b[1]));
+}
+__device__ __forceinline__ float max_xor16_32(float v) {
+  return reduce_xor16_32(v, [](float x, float y) { return fmaxf(x, y); });
+}
+__device__ __forceinline__ float min_xor16_32(float v) {
+  return reduce_xor16_32(v, [](float x, float y) { return fminf(x, y); });
+}
+__device__ __forceinline__ float sum_xor16_32(float v) {
+  return reduce_xor16_32(v, [](float x, float y) { return x + y; });
+}
+
 // Lane exchange within a wave64 (ds_bpermute based).
 __device__ __forceinline__ float shfl_xor(float v, int mask) {
   int lane = __lane_id();

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep it scalar
   const int l16 = lane & 15;
   const int lq = lane >> 4;  // 0..3
 
@@ -152,12 +152,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   // partial tile, lanes whose row lies past S copy nothing; those LDS rows
   // keep earlier finite data (the buffers start zeroed) and are masked.
   auto issue_tile = [&](char (*__restrict__ dst)[P::kTileBytes], int n0) __attribute__((always_inline)) {
+    const bool full = n0 + BN <= S;
 #pragma unroll
     for (int c = 0; c < P::kDmaPerWave; ++c) {
       const int n = wave + c * P::kWaves;
       const int cg = n / P::kRowGroups, r0 = 16 * (n % P::kRowGroups);
       const size_t uni = (size_t)(n0 + r0) * row_bytes + 64u * cg;  // wave-uniform
-      if (n0 + r0 + (int)dma_rl < S) {
+      if (full || n0 + r0 + (int)dma_rl < S) {
         __builtin_amdgcn_global_load_lds(kbase + uni + dma_klane, G2_LDS(&dst[0][n * 1024]), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(vbase + uni + dma_vlane, G2_LDS(&dst[1][n * 1024]), 16, 0, 0);
       }
@@ -182,6 +183,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   float m_run[2] = {kNegInf, kNegInf};
   float l_run[2] = {0.f, 0.f};
   const float k_in = a.cap.k_in, c_out = a.cap.c_out;
+  const int win = a.window;
 
   auto compute_tile = [&](const char (*__restrict__ buf)[P::kTileBytes], int n0) __attribute__((always_inline)) {
     if (!wave_active || n0 > w_p_last || n0 + BN - 1 < w_j_lo) return;
@@ -192,10 +194,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
 
     // ---- S^T = K * Q^T; K operand: row kb*16 + l16, logical chunk 4*kk + lq
     f32x4 st[P::kNB][2];
-#pragma unroll
-    for (int kb = 0; kb < P::kNB; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) st[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < P::kKK; ++kk) {
 #pragma unroll
@@ -203,7 +202,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + kk * (BN * 64) + kb * 1024 + k_lane);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          st[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][kk], st[kb][qb], 0, 0, 0);
+          st[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][kk], kk == 0 ? zero4 : st[kb][qb], 0, 0, 0);
       }
     }
 
@@ -220,10 +219,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
           if constexpr (CAP == kCapFast) z = rcp_fast(1.0f + exp2_fast(x * k_in));
           else if constexpr (CAP == kCapAccurate) z = capped_log2_accurate(x, k_in, c_out);
           else z = x * k_in;
-          if (need_mask) {
+          if (need_mask) {  // wave-uniform branch; the test itself is branch-free
             const int j = n0 + kb * 16 + lq * 4 + i;
             const int p = t0 + qb * 16 + l16 + off;
-            const bool vis = (j <= p) && (j < S) && (!a.is_local || j > p - a.window);
+            const bool vis = (j <= p) & (j < S) & ((j > p - win) | !a.is_local);
             if constexpr (CAP == kCapFast) z = vis ? z : __builtin_inff();
             else z = vis ? z : kNegInf;
           }
@@ -242,8 +241,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
         for (int kb = 0; kb < P::kNB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) rmin = fminf(rmin, st[kb][qb][i]);
-        rmin = fminf(rmin, shfl_xor(rmin, 16));
-        rmin = fminf(rmin, shfl_xor(rmin, 32));
+        rmin = min_xor16_32(rmin);
         mt = __builtin_fmaf(-2.0f * c_out, rmin, c_out);  // -inf when all masked
       } else {
         mt = kNegInf;
@@ -251,8 +249,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
         for (int kb = 0; kb < P::kNB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) mt = fmaxf(mt, st[kb][qb][i]);
-        mt = fmaxf(mt, shfl_xor(mt, 16));
-        mt = fmaxf(mt, shfl_xor(mt, 32));
+        mt = max_xor16_32(mt);
       }
       const bool grow = mt > m_run[qb] + kTau;  // true also for the first visible keys
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {
@@ -351,9 +348,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   // ---- epilogue: O = O^T / l, bf16, store 4 consecutive dims per lane and block
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    float lt = l_run[qb];
-    lt += shfl_xor(lt, 16);
-    lt += shfl_xor(lt, 32);
+    const float lt = sum_xor16_32(l_run[qb]);
     const float inv = 1.0f / lt;
     const int t = t0 + qb * 16 + l16;
     if (t < T) {
