@@ -195,40 +195,55 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
     // ---- S^T = K * Q^T; K operand: row kb*16 + l16, logical chunk 4*kk + lq
     f32x4 st[P::kNB][2];
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 kf[2][P::kNB];  // [parity][kb]: fragments of k-step kk are read one step ahead
+#pragma unroll
+    for (int kb = 0; kb < P::kNB; ++kb)
+      kf[0][kb] = *reinterpret_cast<const bf16x8*>(kt + kb * 1024 + k_lane);
 #pragma unroll
     for (int kk = 0; kk < P::kKK; ++kk) {
+      if (kk + 1 < P::kKK) {
+#pragma unroll
+        for (int kb = 0; kb < P::kNB; ++kb)
+          kf[(kk + 1) & 1][kb] = *reinterpret_cast<const bf16x8*>(kt + (kk + 1) * (BN * 64) + kb * 1024 + k_lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the next step's reads ahead of these MFMAs
 #pragma unroll
       for (int kb = 0; kb < P::kNB; ++kb) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + kk * (BN * 64) + kb * 1024 + k_lane);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          st[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][kk], kk == 0 ? zero4 : st[kb][qb], 0, 0, 0);
+          st[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk & 1][kb], qf[qb][kk], kk == 0 ? zero4 : st[kb][qb], 0, 0, 0);
       }
     }
 
     // ---- soft-cap + mask.  Fast form keeps r = 1/(1+e^{2y}) (s = C - 2C r,
     // decreasing in r; masked: r = +inf); other forms keep s (masked: -inf).
+    // The mask test runs only on tiles that cross the band's edges.
+    auto cap_of = [&](float x) __attribute__((always_inline)) {
+      if constexpr (CAP == kCapFast) return rcp_fast(1.0f + exp2_fast(x * k_in));
+      else if constexpr (CAP == kCapAccurate) return capped_log2_accurate(x, k_in, c_out);
+      else return x * k_in;
+    };
+    constexpr float kMasked = (CAP == kCapFast) ? __builtin_inff() : -__builtin_inff();
+    if (need_mask) {
 #pragma unroll
-    for (int kb = 0; kb < P::kNB; ++kb) {
+      for (int kb = 0; kb < P::kNB; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = st[kb][qb][i];
-          float z;
-          if constexpr (CAP == kCapFast) z = rcp_fast(1.0f + exp2_fast(x * k_in));
-          else if constexpr (CAP == kCapAccurate) z = capped_log2_accurate(x, k_in, c_out);
-          else z = x * k_in;
-          if (need_mask) {  // wave-uniform branch; the test itself is branch-free
+          for (int i = 0; i < 4; ++i) {
             const int j = n0 + kb * 16 + lq * 4 + i;
             const int p = t0 + qb * 16 + l16 + off;
             const bool vis = (j <= p) & (j < S) & ((j > p - win) | !a.is_local);
-            if constexpr (CAP == kCapFast) z = vis ? z : __builtin_inff();
-            else z = vis ? z : kNegInf;
+            const float z = cap_of(st[kb][qb][i]);
+            st[kb][qb][i] = vis ? z : kMasked;
           }
-          st[kb][qb][i] = z;
-        }
-      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < P::kNB; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) st[kb][qb][i] = cap_of(st[kb][qb][i]);
     }
 
     // ---- online softmax (per lane: two query columns)
@@ -300,16 +315,22 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
         w[3] = pack_bf16x2(st[2 * ks + 1][qb][2], st[2 * ks + 1][qb][3]);
         pf[qb] = __builtin_bit_cast(bf16x8, w);
       }
-#pragma unroll
-      for (int db = 0; db < P::kDB; ++db) {
+      auto read_v = [&](int db) __attribute__((always_inline)) {
         const char* vb = vt + (db >> 1) * (BN * 64) + (32 * ks) * 64 + ((db & 1) ? v_lane1 : v_lane0);
         const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G2_LDS_S16X4(vb));
         const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G2_LDS_S16X4(vb + 16 * 64));
         const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, vv);
+        return __builtin_bit_cast(bf16x8, vv);
+      };
+      bf16x8 vf[2];
+      vf[0] = read_v(0);
+#pragma unroll
+      for (int db = 0; db < P::kDB; ++db) {
+        if (db + 1 < P::kDB) vf[(db + 1) & 1] = read_v(db + 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb], o[db][qb], 0, 0, 0);
+          o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db & 1], pf[qb], o[db][qb], 0, 0, 0);
       }
     }
   };
