@@ -36,27 +36,22 @@ struct DecodeArgs {
   float* ws_acc;
 };
 
+// 16-byte vector of the storage type, kept raw until used.
 template <typename E>
 struct Vec16;
 template <>
 struct Vec16<bf16> {
   static constexpr int N = 8;
-  __device__ static void load(const bf16* p, float (&x)[8]) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = bf16_lo_to_f32(w[i]);
-      x[2 * i + 1] = bf16_hi_to_f32(w[i]);
-    }
+  __device__ static float get(const u32x4& w, int e) {
+    return (e & 1) ? bf16_hi_to_f32(w[e >> 1]) : bf16_lo_to_f32(w[e >> 1]);
   }
 };
 template <>
 struct Vec16<float> {
   static constexpr int N = 4;
-  __device__ static void load(const float* p, float (&x)[4]) {
-    const f32x4 w = *reinterpret_cast<const f32x4*>(p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = w[i];
+  __device__ static float get(const u32x4& w, int e) {
+    const f32x4 f = __builtin_bit_cast(f32x4, w);
+    return f[e];
   }
 };
 
@@ -69,15 +64,16 @@ __device__ __forceinline__ bool decode_len_ok(int L, int S, int window, int is_l
 template <typename E, int D, int G>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   constexpr int VEC = Vec16<E>::N;
-  constexpr int LPK = D / VEC;   // lanes per key row
-  constexpr int KPI = 64 / LPK;  // keys per wave step
-  constexpr int UNR = 4;         // keys in flight per lane group
+  constexpr int LPK = D / VEC;   // lanes per key row (16-byte loads)
+  constexpr int KPI = 64 / LPK;  // keys per wave per load instruction
+  constexpr int UNR = 4;         // keys per lane group per batch
   static_assert(LPK <= 64 && 64 % LPK == 0, "key row must fit a wave");
 
   __shared__ float sm_m[4][G], sm_l[4][G];
   __shared__ float sm_acc[4][G][D];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = lane / LPK, sub = lane % LPK;
   const int split = blockIdx.x;
   const int bg = blockIdx.y;
@@ -100,7 +96,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const E* qbase = static_cast<const E*>(a.q) + ((size_t)b * a.H + (size_t)g * G) * D + sub * VEC;
   float qv[G][VEC];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) Vec16<E>::load(qbase + hh * D, qv[hh]);
+  for (int hh = 0; hh < G; ++hh) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(qbase + hh * D);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) qv[hh][e] = Vec16<E>::get(w, e);
+  }
 
   const size_t row_stride = (size_t)a.KVH * D;
   const E* kb = static_cast<const E*>(a.k) + ((size_t)b * S * a.KVH + g) * D + sub * VEC;
@@ -116,37 +116,42 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   }
 
   const int c0_slot = c0 % S;
-  constexpr int kStep = 4 * KPI * UNR;  // positions per workgroup step
-  for (int base = c0 + wave * KPI * UNR; base < c1; base += kStep) {
-    float kx[UNR][VEC], vx[UNR][VEC];
-    bool in[UNR];
+  constexpr int kWaveStep = KPI * UNR;      // positions per wave per batch
+  constexpr int kStep = 4 * kWaveStep;      // positions per workgroup per batch
+  u32x4 kraw[2][UNR], vraw[2][UNR];
+
+  // Loads of one batch (positions base + u*KPI + grp); positions past c1 load nothing.
+  auto load_batch = [&](u32x4 (&kr)[UNR], u32x4 (&vr)[UNR], int base) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int pos = base + u * KPI + grp;
-      in[u] = pos < c1;
       int slot = c0_slot + (pos - c0);
       if (slot >= S) slot -= S;
-      if (in[u]) {
-        Vec16<E>::load(kb + (size_t)slot * row_stride, kx[u]);
-        Vec16<E>::load(vb + (size_t)slot * row_stride, vx[u]);
+      if (pos < c1) {
+        kr[u] = *reinterpret_cast<const u32x4*>(kb + (size_t)slot * row_stride);
+        vr[u] = *reinterpret_cast<const u32x4*>(vb + (size_t)slot * row_stride);
       } else {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) kx[u][e] = vx[u][e] = 0.f;
+        kr[u] = u32x4{0u, 0u, 0u, 0u};
+        vr[u] = u32x4{0u, 0u, 0u, 0u};
       }
     }
+  };
+  // Logits, soft-cap, online softmax and value accumulation of one batch.
+  auto compute_batch = [&](const u32x4 (&kr)[UNR], const u32x4 (&vr)[UNR], int base) __attribute__((always_inline)) {
     float s2[UNR][G];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u)
+    for (int u = 0; u < UNR; ++u) {
+      const bool in = base + u * KPI + grp < c1;
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         float d = 0.f;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) d = __builtin_fmaf(qv[hh][e], kx[u][e], d);
-#pragma unroll
-        for (int mk = LPK / 2; mk >= 1; mk >>= 1) d += shfl_xor(d, mk);
+        for (int e = 0; e < VEC; ++e) d = __builtin_fmaf(qv[hh][e], Vec16<E>::get(kr[u], e), d);
+        d = group_sum<LPK>(d);
         const float s = capped_log2(a.cap.mode, d, a.cap.k_in, a.cap.c_out);
-        s2[u][hh] = in[u] ? s : kNegInf;
+        s2[u][hh] = in ? s : kNegInf;
       }
+    }
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       float mb = s2[0][hh];
@@ -167,11 +172,24 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       for (int e = 0; e < VEC; ++e) {
         float x = acc[hh][e] * alpha;
 #pragma unroll
-        for (int u = 0; u < UNR; ++u) x = __builtin_fmaf(p[u], vx[u][e], x);
+        for (int u = 0; u < UNR; ++u) x = __builtin_fmaf(p[u], Vec16<E>::get(vr[u], e), x);
         acc[hh][e] = x;
       }
       m[hh] = m_new;
     }
+  };
+
+  // Software pipeline: batch i+1's loads are in flight while batch i is computed.
+  int base = c0 + wave * kWaveStep;
+  if (base < c1) load_batch(kraw[0], vraw[0], base);
+  while (base < c1) {
+    if (base + kStep < c1) load_batch(kraw[1], vraw[1], base + kStep);
+    compute_batch(kraw[0], vraw[0], base);
+    base += kStep;
+    if (base >= c1) break;
+    if (base + kStep < c1) load_batch(kraw[0], vraw[0], base + kStep);
+    compute_batch(kraw[1], vraw[1], base);
+    base += kStep;
   }
 
   // ---- merge the KPI lane groups of this wave

@@ -129,6 +129,30 @@ __device__ __forceinline__ float sum_xor16_32(float v) {
   return reduce_xor16_32(v, [](float x, float y) { return x + y; });
 }
 
+// All-reduce (sum) over aligned groups of N lanes (N = 1..64, power of two),
+// built from DPP lane swizzles and the gfx950 row / half-wave swaps, all plain
+// VALU: xor 1 and xor 2 within a quad (quad_perm), then the 8-lane half-row
+// mirror (pairs quad 0 with quad 1), the 16-lane row mirror (pairs the two
+// halves of a row), then the 16- and 32-lane swaps.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N >= 2) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  if constexpr (N >= 4) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  if constexpr (N >= 8) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+  if constexpr (N >= 16) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+  if constexpr (N >= 32) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    auto a = __builtin_amdgcn_permlane16_swap(u, opaque_copy(u), false, false);
+    v = __builtin_bit_cast(float, (unsigned)a[0]) + __builtin_bit_cast(float, (unsigned)a[1]);
+  }
+  if constexpr (N >= 64) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    auto b = __builtin_amdgcn_permlane32_swap(u, opaque_copy(u), false, false);
+    v = __builtin_bit_cast(float, (unsigned)b[0]) + __builtin_bit_cast(float, (unsigned)b[1]);
+  }
+  return v;
+}
+
 // Lane exchange within a wave64 (ds_bpermute based).
 __device__ __forceinline__ float shfl_xor(float v, int mask) {
   int lane = __lane_id();

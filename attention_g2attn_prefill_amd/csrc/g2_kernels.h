@@ -30,7 +30,7 @@ struct DecodeLaunch {
 };
 
 // Keys handled by one split-K workgroup of the decode kernel.
-constexpr int kDecodeChunk = 256;
+constexpr int kDecodeChunk = 512;
 
 inline int decode_splits(int S) { return (S + kDecodeChunk - 1) / kDecodeChunk; }
 

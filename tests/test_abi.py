@@ -61,8 +61,8 @@ def test_check_args(args, expect):
 
 
 def test_workspace_bytes():
-    # splits of 256 positions; per (sequence, head, split): max, sum, d floats
-    assert g2.decode_workspace_bytes(64, 16, 256, 8192) == 64 * 16 * 32 * (2 + 256) * 4
+    # splits of 512 positions; per (sequence, head, split): max, sum, d floats
+    assert g2.decode_workspace_bytes(64, 16, 256, 8192) == 64 * 16 * 16 * (2 + 256) * 4
     assert g2.decode_workspace_bytes(1, 1, 64, 1) == 1 * 1 * 1 * 66 * 4
     assert g2.decode_workspace_bytes(0, 16, 256, 8192) == 0
 
