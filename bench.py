@@ -35,13 +35,19 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_9b_8k_traffic.txt")
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-rows", type=int, default=40960,
                     help="rows per layer of the oracle's bounded CPU sample (0: none)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, run one device copy of this many MiB "
                          "(reference kernel for HBM counter calibration)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no benchmark: read rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE "
+                         "counter CSVs of a run made with --copy-calibration-mib, and "
+                         "write the per-launch HBM traffic of the kernels to profiles/")
+    ap.add_argument("--calibration-mib", type=int, default=1024,
+                    help="size of the calibration copy used in the counter runs")
     return ap.parse_args()
 
 
@@ -65,9 +71,43 @@ def prefill_pairs(T, S, window, is_local):
     return tot
 
 
-def measured_traffic(src_hash):
-    """HBM bytes per prefill launch from committed counter runs, if they were
-    taken on the current kernel sources; else None."""
+def prefill_tile_pairs(T, S, window, is_local, rows_per_wave=32, bn=32):
+    """(query, key) pairs the prefill kernel computes for one (batch, head) slice:
+    every key tile of bn keys that any of a wave's rows_per_wave positions sees
+    is computed whole (masked entries included)."""
+    off = S - T
+    tot = 0
+    for a in range(0, T, rows_per_wave):
+        rows = min(rows_per_wave, T - a)
+        p_first, p_last = a + off, a + rows - 1 + off
+        lo = max(0, p_first - window + 1) if is_local else 0
+        tiles = p_last // bn - lo // bn + 1
+        tot += tiles * bn * rows
+    return tot
+
+
+def copy_gbs(dev, mib=1024, reps=5):
+    """Device-to-device copy rate (read + write bytes / time) on this GPU, for context."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    secs = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    return 2.0 * n / secs / 1e9
+
+
+def measured_traffic(src_hash, key="traffic_bytes_per_launch"):
+    """HBM bytes per launch from committed counter runs, if they were taken on
+    the current kernel sources; else None."""
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.loads(fh.read())
@@ -75,7 +115,60 @@ def measured_traffic(src_hash):
         return None
     if rec.get("source_sha256") != src_hash:
         return None
-    return rec.get("traffic_bytes_per_launch")
+    return rec.get(key)
+
+
+def _counter_rows(path, counter):
+    import csv
+    rows = []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] == counter:
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    return sorted(rows)
+
+
+def write_traffic(fetch_csv, write_csv, calib_mib):
+    """Per-launch HBM bytes of the prefill and decode kernels from counter runs.
+
+    FETCH_SIZE / WRITE_SIZE are in KiB per dispatch.  Each is scaled by the
+    ratio true bytes / counter reading of the calibration copy (the largest
+    device copy in the run: it reads and writes calib_mib MiB)."""
+    fetch = _counter_rows(fetch_csv, "FETCH_SIZE")
+    write = _counter_rows(write_csv, "WRITE_SIZE")
+    nbytes = calib_mib * 1024.0 * 1024.0
+    cf = max((v for _, n, v in fetch if "copyBuffer" in n), default=0.0)
+    cw = max((v for _, n, v in write if "copyBuffer" in n), default=0.0)
+    if cf <= 0 or cw <= 0:
+        raise SystemExit("no calibration copy found in the counter files")
+    f_fetch = nbytes / (cf * 1024.0)
+    f_write = nbytes / (cw * 1024.0)
+
+    def per_launch(tag):
+        fv = [v for _, n, v in fetch if tag in n]
+        wv = [v for _, n, v in write if tag in n]
+        if not fv or not wv:
+            return None
+        return (sum(fv) / len(fv) * 1024.0 * f_fetch + sum(wv) / len(wv) * 1024.0 * f_write,
+                len(fv))
+    pre = per_launch("prefill_bf16_kernel")
+    dec = per_launch("decode_split_kernel")
+    rec = {"source_sha256": kernel_source_hash(),
+           "calibration_copy_mib": calib_mib,
+           "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4),
+           "traffic_bytes_per_launch": round(pre[0]) if pre else None,
+           "prefill_launches": pre[1] if pre else 0,
+           "decode_split_traffic_bytes_per_launch": round(dec[0]) if dec else None,
+           "commands": [
+               "rocprofv3 --pmc FETCH_SIZE -d <dir> -o p --output-format csv -- python3 bench.py "
+               f"--steps 1 --warmup 1 --cpu-rows 0 --copy-calibration-mib {calib_mib}",
+               "rocprofv3 --pmc WRITE_SIZE -d <dir> -o p --output-format csv -- python3 bench.py "
+               f"--steps 1 --warmup 1 --cpu-rows 0 --copy-calibration-mib {calib_mib}",
+               "python3 bench.py --write-traffic <fetch csv> <write csv>"]}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write(json.dumps(rec, indent=1) + "\n")
+    print(json.dumps(rec))
 
 
 def cpu_baseline(cfg, q, k, v, rows_per_layer):
@@ -107,6 +200,9 @@ def cpu_baseline(cfg, q, k, v, rows_per_layer):
 
 def main():
     args = parse_args()
+    if args.write_traffic:
+        write_traffic(args.write_traffic[0], args.write_traffic[1], args.calibration_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build "
               "measures the single-GPU kernels and has no multi-GPU path.", file=sys.stderr)
@@ -182,7 +278,10 @@ def main():
     ms = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(4)]
                    for i in range(args.steps)])  # per step: pl, pg, dl, dg (ms)
     t_pl, t_pg, t_dl, t_dg = ms.mean(axis=0) * 1e-3
+    med = np.median(ms, axis=0)
+    mn = ms.min(axis=0)
 
+    copy_rate = copy_gbs(dev)
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -196,6 +295,9 @@ def main():
     f_local = 4.0 * d * B * H * prefill_pairs(T, S, W, True)
     f_global = 4.0 * d * B * H * prefill_pairs(T, S, W, False)
     prefill_tflops = (f_local + f_global) / (t_pl + t_pg) / 1e12
+    bn = 32 if d > 128 else 64
+    ft_local = 4.0 * d * B * H * prefill_tile_pairs(T, S, W, True, bn=bn)
+    ft_global = 4.0 * d * B * H * prefill_tile_pairs(T, S, W, False, bn=bn)
     row_bytes = 2 * DKVH * Dd * 2  # K and V bytes per visible position (bf16)
     n_local = np.minimum(lens.astype(np.int64), cfg_d["window"]).sum()
     n_global = lens.astype(np.int64).sum()
@@ -213,13 +315,22 @@ def main():
               "frac_of_hbm_peak": round(decode_gbs / PEAK_HBM_GBS, 4),
               "roofline": {"bound": "hbm", "achieved": round(decode_gbs, 1),
                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                           "frac": round(decode_gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                           "frac": round(decode_gbs / PEAK_HBM_GBS, 4),
+                           "traffic": measured_traffic(src_hash, "decode_split_traffic_bytes_per_launch")},
               "ms_local": round(t_dl * 1e3, 4), "ms_global": round(t_dg * 1e3, 4),
-              "bytes_local": b_local, "bytes_global": b_global}
+              "ms_local_median_min": [round(med[2], 4), round(mn[2], 4)],
+              "ms_global_median_min": [round(med[3], 4), round(mn[3], 4)],
+              "bytes_local": b_local, "bytes_global": b_global,
+              "device_copy_gbs_context": round(copy_rate, 1)}
     per_layer = {"prefill_local_ms": round(t_pl * 1e3, 4), "prefill_global_ms": round(t_pg * 1e3, 4),
                  "prefill_local_tflops": round(f_local / t_pl / 1e12, 2),
                  "prefill_global_tflops": round(f_global / t_pg / 1e12, 2),
-                 "prefill_flops_local": f_local, "prefill_flops_global": f_global}
+                 "prefill_local_ms_median_min": [round(med[0], 4), round(mn[0], 4)],
+                 "prefill_global_ms_median_min": [round(med[1], 4), round(mn[1], 4)],
+                 "prefill_flops_local": f_local, "prefill_flops_global": f_global,
+                 "prefill_tile_level_flops_local": ft_local,
+                 "prefill_tile_level_flops_global": ft_global,
+                 "prefill_tile_level_tflops": round((ft_local + ft_global) / (t_pl + t_pg) / 1e12, 2)}
 
     cpu = None
     if args.cpu_rows > 0:
