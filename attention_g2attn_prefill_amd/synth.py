@@ -177,6 +177,44 @@ def decode_inputs(cfg: dict, *, poison: bool = False):
     return q, k_g, v_g, lens, k_l, v_l
 
 
+def paged_from_linear(cache: torch.Tensor, lens: np.ndarray, block_size: int, *,
+                      seed: int, keep_last: int = 0, spare_blocks: int = 0,
+                      fill=float("nan")):
+    """Lay a linear cache out as a block pool and a block table.
+
+    cache: (B, S, KVH, d) holding position p of sequence b at row p.  Logical
+    block i of sequence b (positions i*block_size .. (i+1)*block_size - 1) is
+    stored in a physical block chosen by a seeded random permutation.  Blocks
+    at or past L_b are not allocated; with keep_last = W > 0, blocks holding
+    none of the last W positions are not allocated either (dropped, as a
+    serving runtime drops a local layer's old blocks).  Unallocated table
+    entries are -1.  Rows of allocated blocks at positions >= L_b, and
+    `spare_blocks` extra pool blocks, are set to `fill`.
+
+    Returns pool (num_blocks, block_size, KVH, d) and table (B, max_blocks)
+    int32 with max_blocks = ceil(S / block_size).
+    """
+    B, S = cache.shape[0], cache.shape[1]
+    bs = block_size
+    max_blocks = (S + bs - 1) // bs
+    wanted = []
+    for b in range(B):
+        L = int(lens[b])
+        first = max(0, L - keep_last) // bs if keep_last > 0 else 0
+        last = (L - 1) // bs
+        wanted.extend((b, i) for i in range(first, last + 1))
+    n = len(wanted) + spare_blocks
+    perm = np.random.default_rng(np.random.SeedSequence([seed, 7])).permutation(n)
+    pool = torch.full((n, bs) + tuple(cache.shape[2:]), fill, dtype=cache.dtype)
+    table = np.full((B, max_blocks), -1, np.int32)
+    for (b, i), phys in zip(wanted, perm[:len(wanted)]):
+        L = int(lens[b])
+        lo, hi = i * bs, min((i + 1) * bs, L, S)
+        table[b, i] = phys
+        pool[phys, :hi - lo] = cache[b, lo:hi]
+    return pool, table
+
+
 def to_f32_numpy(t: torch.Tensor) -> np.ndarray:
     """Exact float32 copy of a CPU/GPU tensor holding bf16 or f32 values."""
     return t.detach().to("cpu", torch.float32).contiguous().numpy()

@@ -50,6 +50,10 @@ def _load():
     lib.g2o_decode.argtypes = [_f32p, _f32p, _f32p, _i32p, _f64p, _I, _I, _I,
                                _I, _I, _D, _D, _I, _I, _i64p, ctypes.c_int64]
     lib.g2o_decode.restype = _I
+    lib.g2o_decode_paged.argtypes = [_f32p, _f32p, _f32p, _i32p, _I, _i32p, _f64p, _I,
+                                     _I, _I, _I, _I, _I, _D, _D, _I, _I, _i64p,
+                                     ctypes.c_int64]
+    lib.g2o_decode_paged.restype = _I
     lib.g2o_threads.argtypes = []
     lib.g2o_threads.restype = _I
     _lib = lib
@@ -177,6 +181,47 @@ def decode(q, k_cache, v_cache, kv_lens, *, query_scale, softcap, window, is_loc
     st = _load().g2o_decode(_ptr(q, _f32p), _ptr(kc, _f32p), _ptr(vc, _f32p),
                             _ptr(lens, _i32p), _ptr(out, _f64p), B, S, H, KVH, d,
                             query_scale, softcap, window, int(bool(is_local)), rp, n)
+    if st != 0:
+        raise OracleError(f"oracle rejected arguments (status {st})")
+    return out
+
+
+def decode_paged(q, k_pool, v_pool, block_table, kv_lens, *, query_scale, softcap,
+                 window, is_local, rows=None):
+    """Decode output in float64 against a paged KV cache.
+
+    q: (B,1,H,d); pools: (num_blocks, block_size, KVH, d); block_table:
+    (B, max_blocks) ints, entry [b][i] = physical block of positions
+    i*block_size .. (i+1)*block_size - 1; kv_lens: (B,) ints in
+    [1, max_blocks*block_size].  Only entries of blocks holding a position the
+    query sees are read; a needed entry outside the pool gives a NaN row.
+    rows=None returns (B,1,H,d); otherwise rows are flat ids b*H + h and the
+    result is (n, d).
+    """
+    q, kp, vp = _f32(q), _f32(k_pool), _f32(v_pool)
+    B, T, H, d = q.shape
+    if T != 1:
+        raise OracleError("decode takes one query token per sequence")
+    NB, BS, KVH = kp.shape[0], kp.shape[1], kp.shape[2]
+    if kp.shape[3] != d or vp.shape != kp.shape:
+        raise OracleError("pool shape mismatch")
+    table = np.ascontiguousarray(np.asarray(block_table, dtype=np.int32))
+    if table.ndim != 2 or table.shape[0] != B:
+        raise OracleError("block_table must be (B, max_blocks)")
+    lens = np.ascontiguousarray(np.asarray(kv_lens, dtype=np.int32))
+    if lens.shape != (B,):
+        raise OracleError("kv_lens must have B entries")
+    if rows is None:
+        out = np.empty((B, 1, H, d), np.float64)
+        rp, n = None, 0
+    else:
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        out = np.empty((rows.size, d), np.float64)
+        rp, n = _ptr(rows, _i64p), rows.size
+    st = _load().g2o_decode_paged(_ptr(q, _f32p), _ptr(kp, _f32p), _ptr(vp, _f32p),
+                                  _ptr(table, _i32p), table.shape[1], _ptr(lens, _i32p),
+                                  _ptr(out, _f64p), B, H, KVH, d, BS, NB, query_scale,
+                                  softcap, window, int(bool(is_local)), rp, n)
     if st != 0:
         raise OracleError(f"oracle rejected arguments (status {st})")
     return out

@@ -272,6 +272,84 @@ int g2o_decode(const float* q, const float* k_cache, const float* v_cache,
   return G2O_OK;
 }
 
+/* Decode against a paged KV cache (Gemma 2 Guide, "Deep Dive" item 2: KV
+ * memory managed in discrete blocks; local layers drop blocks older than the
+ * window).  k_pool, v_pool: (num_blocks, block_size, KVH, d); block_table:
+ * (B, max_blocks) int32, entry [b][i] = physical block holding positions
+ * i*block_size .. (i+1)*block_size - 1 of sequence b.  The query of sequence
+ * b sits at position L_b - 1 and sees the keys the prefill mask allows; only
+ * those positions are looked up, so table entries of other blocks (evicted or
+ * unused) are never read.  1 <= L_b <= max_blocks * block_size.  A needed
+ * entry outside [0, num_blocks) makes that row's output NaN.
+ * rows == NULL: every (b, h), out is (B,1,H,d); else rows r = b*H + h. */
+int g2o_decode_paged(const float* q, const float* k_pool, const float* v_pool,
+                     const int32_t* block_table, int max_blocks,
+                     const int32_t* kv_lens, double* out, int B, int H, int KVH,
+                     int d, int block_size, int num_blocks, double query_scale,
+                     double softcap, int window, int is_local,
+                     const int64_t* rows, int64_t nrows) {
+  if (B <= 0 || H <= 0 || KVH <= 0 || d <= 0 || H % KVH != 0) return G2O_ERR_ARG;
+  if (block_size <= 0 || max_blocks <= 0 || num_blocks <= 0) return G2O_ERR_ARG;
+  if (is_local && window < 1) return G2O_ERR_ARG;
+  const int64_t cap_len = (int64_t)max_blocks * block_size;
+  int64_t maxL = 0;
+  for (int b = 0; b < B; ++b) {
+    if (kv_lens[b] < 1 || kv_lens[b] > cap_len) return G2O_ERR_ARG;
+    if (kv_lens[b] > maxL) maxL = kv_lens[b];
+  }
+  const int64_t total = (int64_t)B * H;
+  const int64_t n = rows ? nrows : total;
+  if (rows) {
+    for (int64_t i = 0; i < n; ++i)
+      if (rows[i] < 0 || rows[i] >= total) return G2O_ERR_ARG;
+  }
+#pragma omp parallel
+  {
+    const float** k_rows = (const float**)malloc(sizeof(float*) * (size_t)maxL);
+    const float** v_rows = (const float**)malloc(sizeof(float*) * (size_t)maxL);
+    unsigned char* allowed = (unsigned char*)malloc((size_t)maxL);
+    double* s = (double*)malloc(sizeof(double) * (size_t)maxL);
+    double* w = (double*)malloc(sizeof(double) * (size_t)maxL);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n; ++i) {
+      const int64_t r = rows ? rows[i] : i;
+      const int h = (int)(r % H);
+      const int b = (int)(r / H);
+      const int g = h / (H / KVH);
+      const int64_t L = kv_lens[b];
+      const int64_t p = L - 1;
+      int bad = 0;
+      for (int64_t j = 0; j < L; ++j) {
+        allowed[j] = (unsigned char)g2o_allowed(p, j, window, is_local);
+        k_rows[j] = v_rows[j] = NULL;
+        if (!allowed[j]) continue;
+        const int64_t blk = block_table[(int64_t)b * max_blocks + j / block_size];
+        if (blk < 0 || blk >= num_blocks) {
+          bad = 1;
+          break;
+        }
+        const int64_t row = (blk * block_size + j % block_size) * KVH + g;
+        k_rows[j] = k_pool + row * d;
+        v_rows[j] = v_pool + row * d;
+      }
+      if (bad) {
+        for (int e = 0; e < d; ++e) out[i * d + e] = NAN;
+        continue;
+      }
+      const float* qrow = q + r * d;
+      row_logits(qrow, k_rows, allowed, L, d, query_scale, softcap, s);
+      row_softmax(s, L, w);
+      row_output(v_rows, w, L, d, out + i * d);
+    }
+    free(k_rows);
+    free(v_rows);
+    free(allowed);
+    free(s);
+    free(w);
+  }
+  return G2O_OK;
+}
+
 /* Number of threads the parallel loops above use (OpenMP's default team). */
 #ifdef _OPENMP
 #include <omp.h>

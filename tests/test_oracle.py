@@ -454,3 +454,88 @@ def test_brute_force_mpmath_tiny():
                                       for j in s)
                     # logits near the cap carry ~ulp(50) = 7e-15 absolute error in fp64
                     assert abs(out[0, t, h, e] - float(ref)) <= 2e-14
+
+
+# ---- paged-KV decode (Guide "Deep Dive" item 2: KV memory managed in blocks;
+# local layers drop blocks older than the window)
+
+def _paged_case(seed, B=3, S=48, H=4, KVH=2, d=8, lens=(1, 21, 48)):
+    q = torch.from_numpy(rand((B, 1, H, d), seed, mul=3.0))
+    kc = torch.from_numpy(rand((B, S, KVH, d), seed + 1))
+    vc = torch.from_numpy(rand((B, S, KVH, d), seed + 2))
+    return q, kc, vc, np.array(lens, np.int32)
+
+
+@pytest.mark.parametrize("block_size", [1, 4, 16, 64])
+@pytest.mark.parametrize("is_local,window", [(False, 4096), (True, 7), (True, 1), (True, 48)])
+def test_decode_paged_equals_linear_cache(block_size, is_local, window):
+    """Where a position's block sits in the pool does not change the result:
+    any block placement gives exactly the (pinned) linear-cache decode, and
+    dropped or unwritten blocks (NaN) are never read."""
+    q, kc, vc, lens = _paged_case(201)
+    kp, tab = synth.paged_from_linear(kc, lens, block_size, seed=3,
+                                      keep_last=window if is_local else 0, spare_blocks=2)
+    vp, tab2 = synth.paged_from_linear(vc, lens, block_size, seed=3,
+                                       keep_last=window if is_local else 0, spare_blocks=2)
+    assert np.array_equal(tab, tab2)
+    kw = dict(query_scale=0.4, softcap=50.0, window=window, is_local=is_local)
+    lin = oracle.decode(q.numpy(), kc.numpy(), vc.numpy(), lens, **kw)
+    got = oracle.decode_paged(q.numpy(), kp.numpy(), vp.numpy(), tab, lens, **kw)
+    assert np.all(np.isfinite(got))
+    assert np.array_equal(got, lin)
+
+
+def test_decode_paged_brute_force():
+    """Independent numpy evaluation of the definition on a scattered pool."""
+    B, H, KVH, d, bs, W = 2, 4, 2, 6, 3, 5
+    rng = np.random.default_rng(211)
+    nb = 9
+    kp = rng.standard_normal((nb, bs, KVH, d)).astype(np.float32)
+    vp = rng.standard_normal((nb, bs, KVH, d)).astype(np.float32)
+    q = (3.0 * rng.standard_normal((B, 1, H, d))).astype(np.float32)
+    tab = np.array([[4, 0, 7, -1], [2, 8, 1, 5]], np.int32)
+    lens = np.array([8, 11], np.int32)
+    qs, cap = 0.6, 5.0
+    for is_local in (False, True):
+        got = oracle.decode_paged(q, kp, vp, tab, lens, query_scale=qs, softcap=cap,
+                                  window=W, is_local=is_local)
+        for b in range(B):
+            L = int(lens[b])
+            js = np.arange(max(0, L - W) if is_local else 0, L)
+            for h in range(H):
+                g = h // (H // KVH)
+                K = np.stack([kp[tab[b, j // bs], j % bs, g] for j in js]).astype(np.float64)
+                V = np.stack([vp[tab[b, j // bs], j % bs, g] for j in js]).astype(np.float64)
+                x = (q[b, 0, h].astype(np.float64) * qs) @ K.T
+                s = cap * np.tanh(x / cap)
+                w = np.exp(s - s.max())
+                w /= w.sum()
+                assert np.max(np.abs(got[b, 0, h] - w @ V)) <= 1e-13
+
+
+def test_decode_paged_bad_block_gives_nan_row():
+    q, kc, vc, lens = _paged_case(221)
+    kp, tab = synth.paged_from_linear(kc, lens, 4, seed=5)
+    vp, _ = synth.paged_from_linear(vc, lens, 4, seed=5)
+    kw = dict(query_scale=0.4, softcap=50.0, window=4096, is_local=False)
+    good = oracle.decode_paged(q.numpy(), kp.numpy(), vp.numpy(), tab, lens, **kw)
+    bad_tab = tab.copy()
+    bad_tab[1, 2] = kp.shape[0]          # a block the query needs, outside the pool
+    bad = oracle.decode_paged(q.numpy(), kp.numpy(), vp.numpy(), bad_tab, lens, **kw)
+    assert np.all(np.isnan(bad[1]))
+    assert np.array_equal(bad[0], good[0]) and np.array_equal(bad[2], good[2])
+    # an entry of a block the query cannot see is never looked up
+    loc = dict(kw, window=5, is_local=True)
+    ref = oracle.decode_paged(q.numpy(), kp.numpy(), vp.numpy(), tab, lens, **loc)
+    far = tab.copy()
+    far[2, 0] = 10 ** 6                   # positions 0..3, outside the window of L = 48
+    assert np.array_equal(oracle.decode_paged(q.numpy(), kp.numpy(), vp.numpy(), far, lens, **loc), ref)
+
+
+def test_decode_paged_rejects_bad_lengths():
+    q, kc, vc, lens = _paged_case(231)
+    kp, tab = synth.paged_from_linear(kc, lens, 8, seed=1)
+    for bad in ([0, 21, 48], [1, 21, 49]):
+        with pytest.raises(oracle.OracleError):
+            oracle.decode_paged(q.numpy(), kp.numpy(), kp.numpy(), tab, np.array(bad, np.int32),
+                                query_scale=1.0, softcap=50.0, window=4, is_local=True)
