@@ -1,4 +1,4 @@
-"""Gemma 2 attention layer for MI355X (gfx950): prefill and decode.
+"""Gemma 2 attention layer for MI355X (gfx950): prefill, decode and paged decode.
 
 The compute path is the C-ABI library libg2attn.so (hand-written HIP kernels);
 this package is a thin ctypes binding over it plus a seeded input generator
@@ -7,6 +7,7 @@ if the library has not been built: there is no CPU fallback.
 """
 _BINDING_NAMES = (
     "prefill", "decode", "decode_workspace_bytes", "check_args", "status_string",
+    "decode_paged", "decode_paged_workspace_bytes", "check_paged_args",
     "library_path", "G2attnError", "lib",
 )
 

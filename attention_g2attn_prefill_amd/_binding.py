@@ -31,6 +31,13 @@ lib.g2attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _I, _I, _I, _I, _I, _I, _
 lib.g2attn_decode.restype = _I
 lib.g2attn_decode_workspace_bytes.argtypes = [_I, _I, _I, _I]
 lib.g2attn_decode_workspace_bytes.restype = ctypes.c_size_t
+lib.g2attn_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _I, _vp, _I, _I, _I, _I, _I, _I,
+                                    _F, _F, _I, _I, _I, _vp, ctypes.c_size_t, _vp]
+lib.g2attn_decode_paged.restype = _I
+lib.g2attn_decode_paged_workspace_bytes.argtypes = [_I] * 5
+lib.g2attn_decode_paged_workspace_bytes.restype = ctypes.c_size_t
+lib.g2attn_check_paged_args.argtypes = [_I] * 10
+lib.g2attn_check_paged_args.restype = _I
 lib.g2attn_check_args.argtypes = [_I] * 10
 lib.g2attn_check_args.restype = _I
 lib.g2attn_status_string.argtypes = [_I]
@@ -58,6 +65,17 @@ def check_args(B, T, S, H, KVH, d, window, is_local, dtype=G2_BF16, decode=False
 
 def decode_workspace_bytes(B, H, d, S) -> int:
     return int(lib.g2attn_decode_workspace_bytes(B, H, d, S))
+
+
+def decode_paged_workspace_bytes(B, H, d, max_blocks, block_size) -> int:
+    return int(lib.g2attn_decode_paged_workspace_bytes(B, H, d, max_blocks, block_size))
+
+
+def check_paged_args(B, H, KVH, d, block_size, max_blocks, num_blocks, window, is_local,
+                     dtype=G2_BF16) -> int:
+    """Host-only validation of paged-decode scalars; the status the call would return."""
+    return lib.g2attn_check_paged_args(B, H, KVH, d, block_size, max_blocks, num_blocks,
+                                       window, int(is_local), dtype)
 
 
 def _stream_handle(stream):
@@ -130,4 +148,46 @@ def decode(q, k_cache, v_cache, kv_lens, *, query_scale, softcap=50.0, window=40
                            workspace.numel() * workspace.element_size(), _stream_handle(stream))
     if st != 0:
         raise G2attnError(st, "g2attn_decode")
+    return out
+
+
+def decode_paged(q, k_pool, v_pool, block_table, kv_lens, *, query_scale, softcap=50.0,
+                 window=4096, is_local, out=None, workspace=None, stream=None):
+    """One query token per sequence against a paged KV cache.
+
+    q (B,1,H,d); k_pool/v_pool (num_blocks, block_size, KVH, d); block_table
+    int32 (B, max_blocks) on the GPU, entry [b][i] = pool block of positions
+    i*block_size .. (i+1)*block_size - 1 (entries of blocks the query cannot
+    see are never read); kv_lens int32 (B,) on the GPU.  workspace: a uint8
+    GPU tensor of at least decode_paged_workspace_bytes(B,H,d,max_blocks,
+    block_size) bytes (allocated here if None).
+    """
+    B, T, H, d = q.shape
+    NB, BS, KVH, dk = k_pool.shape
+    if T != 1 or dk != d or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("shape mismatch between q and the pools")
+    if q.dtype not in _DTYPES or k_pool.dtype != q.dtype or v_pool.dtype != q.dtype:
+        raise TypeError("q and pools must share dtype bfloat16 or float32")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise TypeError("block_table must be int32 of shape (B, max_blocks)")
+    if kv_lens.dtype != torch.int32 or tuple(kv_lens.shape) != (B,):
+        raise TypeError("kv_lens must be int32 of shape (B,)")
+    max_blocks = block_table.shape[1]
+    if workspace is None:
+        need = decode_paged_workspace_bytes(B, H, d, max_blocks, BS)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q's shape and dtype")
+    st = lib.g2attn_decode_paged(_dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                                 _dev(out, "out"), _dev(block_table, "block_table"), max_blocks,
+                                 _dev(kv_lens, "kv_lens"), B, H, KVH, d, BS, NB,
+                                 float(query_scale), float(softcap), int(window),
+                                 int(bool(is_local)), _DTYPES[q.dtype],
+                                 _dev(workspace, "workspace"),
+                                 workspace.numel() * workspace.element_size(),
+                                 _stream_handle(stream))
+    if st != 0:
+        raise G2attnError(st, "g2attn_decode_paged")
     return out

@@ -29,6 +29,28 @@ int check_scalars(int B, int T, int S, int H, int KVH, int d, int window, int is
   return G2_OK;
 }
 
+int check_paged_scalars(int B, int H, int KVH, int d, int block_size, int max_blocks,
+                        int num_blocks, int window, int is_local, int dtype) {
+  if (B <= 0 || H <= 0 || KVH <= 0 || d <= 0) return G2_ERR_ARG;
+  if (block_size <= 0 || max_blocks <= 0 || num_blocks <= 0) return G2_ERR_ARG;
+  if ((block_size & (block_size - 1)) != 0 || block_size > 65536) return G2_ERR_ARG;
+  if ((long long)max_blocks * block_size >= (1LL << 31)) return G2_ERR_ARG;
+  if (dtype != G2_BF16 && dtype != G2_F32) return G2_ERR_ARG;
+  if (H % KVH != 0) return G2_ERR_ARG;
+  if (is_local != 0 && is_local != 1) return G2_ERR_ARG;
+  if (is_local && window < 1) return G2_ERR_ARG;
+  if (d != 64 && d != 128 && d != 256) return G2_ERR_UNSUPPORTED;
+  const int G = H / KVH;
+  if (G != 1 && G != 2) return G2_ERR_UNSUPPORTED;
+  return G2_OK;
+}
+
+size_t paged_workspace_bytes(int B, int H, int d, int max_blocks, int block_size) {
+  const long long cap = (long long)max_blocks * block_size;
+  const size_t splits = (size_t)((cap + g2::kDecodeChunk - 1) / g2::kDecodeChunk);
+  return (size_t)B * H * splits * (2 + (size_t)d) * sizeof(float);
+}
+
 }  // namespace
 
 extern "C" {
@@ -81,6 +103,42 @@ int g2attn_decode(const void* q, const void* k_cache, const void* v_cache, void*
   if (!aligned16(workspace)) return G2_ERR_ALIGN;
   g2::DecodeLaunch L{q, k_cache, v_cache, out, kv_lens, B, S, H, KVH, d,
                      query_scale, softcap, window, is_local, workspace};
+  const hipError_t e = g2::launch_decode(L, dtype, stream);
+  return e == hipSuccess ? G2_OK : G2_ERR_LAUNCH;
+}
+
+int g2attn_check_paged_args(int B, int H, int KVH, int d, int block_size, int max_blocks,
+                            int num_blocks, int window, int is_local, int dtype) {
+  return check_paged_scalars(B, H, KVH, d, block_size, max_blocks, num_blocks, window, is_local,
+                             dtype);
+}
+
+size_t g2attn_decode_paged_workspace_bytes(int B, int H, int d, int max_blocks, int block_size) {
+  if (B <= 0 || H <= 0 || d <= 0 || max_blocks <= 0 || block_size <= 0) return 0;
+  if ((long long)max_blocks * block_size >= (1LL << 31)) return 0;
+  return paged_workspace_bytes(B, H, d, max_blocks, block_size);
+}
+
+int g2attn_decode_paged(const void* q, const void* k_pool, const void* v_pool, void* out,
+                        const int32_t* block_table, int max_blocks, const int32_t* kv_lens,
+                        int B, int H, int KVH, int d, int block_size, int num_blocks,
+                        float query_scale, float softcap, int window, int is_local, int dtype,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_paged_scalars(B, H, KVH, d, block_size, max_blocks, num_blocks, window,
+                               is_local, dtype);
+  if (st != G2_OK) return st;
+  if (!q || !k_pool || !v_pool || !out || !block_table || !kv_lens) return G2_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+    return G2_ERR_ALIGN;
+  g2::DecodeLaunch L{q, k_pool, v_pool, out, kv_lens, B, 1, H, KVH, d,
+                     query_scale, softcap, window, is_local, workspace};
+  L.block_table = block_table;
+  L.max_blocks = max_blocks;
+  L.block_size = block_size;
+  L.num_blocks = num_blocks;
+  const size_t need = (size_t)B * H * g2::decode_call_splits(L) * (2 + (size_t)d) * sizeof(float);
+  if (!workspace || workspace_bytes < need) return G2_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return G2_ERR_ALIGN;
   const hipError_t e = g2::launch_decode(L, dtype, stream);
   return e == hipSuccess ? G2_OK : G2_ERR_LAUNCH;
 }

@@ -17,6 +17,12 @@
 //  * groups, then waves (through LDS), are merged at the end, and each split
 //    writes (max, sum, unnormalised accumulator) to the workspace;
 //  * a second kernel merges the splits of every (sequence, head).
+//
+// Paged mode (Gemma 2 Guide, "Deep Dive" item 2: block-managed KV memory,
+// local layers dropping blocks older than the window): K and V live in a pool
+// of fixed-size blocks and a per-sequence table maps logical block i to a
+// pool block.  Each split stages the table entries of the blocks it covers in
+// LDS once and checks them; the loads then address pool rows through them.
 #include "g2_device.h"
 #include "g2_kernels.h"
 
@@ -34,6 +40,9 @@ struct DecodeArgs {
   float* ws_m;
   float* ws_l;
   float* ws_acc;
+  // paged mode
+  const int32_t* table;
+  int max_blocks, bs_log2, num_blocks;
 };
 
 // 16-byte vector of the storage type, kept raw until used.
@@ -61,7 +70,14 @@ __device__ __forceinline__ bool decode_len_ok(int L, int S, int window, int is_l
   return seen <= S;
 }
 
-template <typename E, int D, int G>
+// Length check of either cache form (paged: the table's capacity).
+template <bool PAGED>
+__device__ __forceinline__ bool decode_len_ok_any(const DecodeArgs& a, int L) {
+  if constexpr (PAGED) return L >= 1 && (long long)L <= ((long long)a.max_blocks << a.bs_log2);
+  else return decode_len_ok(L, a.S, a.window, a.is_local);
+}
+
+template <typename E, int D, int G, bool PAGED>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   constexpr int VEC = Vec16<E>::N;
   constexpr int LPK = D / VEC;   // lanes per key row (16-byte loads)
@@ -71,6 +87,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 
   __shared__ float sm_m[4][G], sm_l[4][G];
   __shared__ float sm_acc[4][G][D];
+  __shared__ int sm_blk[PAGED ? kDecodeChunk + 1 : 1];  // pool blocks of this split
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -80,7 +97,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int b = bg / a.KVH, g = bg % a.KVH;
   const int S = a.S;
   const int L = a.kv_lens[b];
-  const bool ok = decode_len_ok(L, S, a.window, a.is_local);
+  const bool ok = decode_len_ok_any<PAGED>(a, L);
   const int lo = a.is_local ? max(0, L - a.window) : 0;
   const int c0 = lo + split * kDecodeChunk;
   const int c1 = min(c0 + kDecodeChunk, L);
@@ -91,6 +108,24 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       a.ws_l[part0 + (size_t)tid * a.nsplit] = 0.f;
     }
     return;
+  }
+  const int bs_log2 = a.bs_log2;
+  const int fb = c0 >> bs_log2;  // first logical block of the split (paged)
+  if constexpr (PAGED) {
+    const int nb = ((c1 - 1) >> bs_log2) - fb + 1;
+    int bad = 0;
+    for (int i = tid; i < nb; i += 256) {
+      const int e = a.table[(size_t)b * a.max_blocks + fb + i];
+      bad |= (e < 0) | (e >= a.num_blocks);
+      sm_blk[i] = e;
+    }
+    if (__syncthreads_or(bad)) {  // a visible position has no pool block: NaN result
+      if (tid < G) {
+        a.ws_m[part0 + (size_t)tid * a.nsplit] = kNegInf;
+        a.ws_l[part0 + (size_t)tid * a.nsplit] = __builtin_nanf("");
+      }
+      return;
+    }
   }
 
   const E* qbase = static_cast<const E*>(a.q) + ((size_t)b * a.H + (size_t)g * G) * D + sub * VEC;
@@ -103,8 +138,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   }
 
   const size_t row_stride = (size_t)a.KVH * D;
-  const E* kb = static_cast<const E*>(a.k) + ((size_t)b * S * a.KVH + g) * D + sub * VEC;
-  const E* vb = static_cast<const E*>(a.v) + ((size_t)b * S * a.KVH + g) * D + sub * VEC;
+  const size_t seq_rows = PAGED ? 0 : (size_t)b * S;  // pools are shared by all sequences
+  const E* kb = static_cast<const E*>(a.k) + (seq_rows * a.KVH + g) * D + sub * VEC;
+  const E* vb = static_cast<const E*>(a.v) + (seq_rows * a.KVH + g) * D + sub * VEC;
 
   float m[G], l[G], acc[G][VEC];
 #pragma unroll
@@ -115,7 +151,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     for (int e = 0; e < VEC; ++e) acc[hh][e] = 0.f;
   }
 
-  const int c0_slot = c0 % S;
+  const int c0_slot = PAGED ? 0 : c0 % S;
   constexpr int kWaveStep = KPI * UNR;      // positions per wave per batch
   constexpr int kStep = 4 * kWaveStep;      // positions per workgroup per batch
   u32x4 kraw[2][UNR], vraw[2][UNR];
@@ -125,8 +161,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int pos = base + u * KPI + grp;
-      int slot = c0_slot + (pos - c0);
-      if (slot >= S) slot -= S;
+      size_t slot;  // row of the cache (ring / linear) or of the pool (paged)
+      if constexpr (PAGED) {
+        slot = 0;
+        if (pos < c1)
+          slot = ((size_t)sm_blk[(pos >> bs_log2) - fb] << bs_log2) | (size_t)(pos & ((1 << bs_log2) - 1));
+      } else {
+        int sl = c0_slot + (pos - c0);
+        if (sl >= S) sl -= S;
+        slot = (size_t)sl;
+      }
       if (pos < c1) {
         kr[u] = *reinterpret_cast<const u32x4*>(kb + (size_t)slot * row_stride);
         vr[u] = *reinterpret_cast<const u32x4*>(vb + (size_t)slot * row_stride);
@@ -247,16 +291,19 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 }
 
 // One workgroup per (sequence, head): merge the splits and write the output.
-template <typename E, int D>
+template <typename E, int D, bool PAGED>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const int bh = blockIdx.x;
   const int b = bh / a.H;
   const int L = a.kv_lens[b];
-  const bool ok = decode_len_ok(L, a.S, a.window, a.is_local);
+  bool ok = decode_len_ok_any<PAGED>(a, L);
   const size_t p0 = (size_t)bh * a.nsplit;
   float mx = kNegInf;
-  for (int s = 0; s < a.nsplit; ++s)
-    if (a.ws_l[p0 + s] > 0.f) mx = fmaxf(mx, a.ws_m[p0 + s]);
+  for (int s = 0; s < a.nsplit; ++s) {
+    const float ls = a.ws_l[p0 + s];
+    if (ls != ls) ok = false;  // a split that could not read its keys
+    if (ls > 0.f) mx = fmaxf(mx, a.ws_m[p0 + s]);
+  }
   float lsum = 0.f;
   for (int s = 0; s < a.nsplit; ++s) {
     const float ls = a.ws_l[p0 + s];
@@ -274,13 +321,19 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   }
 }
 
-template <typename E, int D, int G>
-static hipError_t launch_decode_t(DecodeArgs a, int B, int KVH, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<E, D, G>), dim3(a.nsplit, B * KVH), dim3(256), 0, stream, a);
+template <typename E, int D, int G, bool PAGED>
+static hipError_t launch_decode_p(DecodeArgs a, int B, int KVH, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_split_kernel<E, D, G, PAGED>), dim3(a.nsplit, B * KVH), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<E, D>), dim3(B * a.H), dim3(D < 256 ? D : 256), 0, stream, a);
+  hipLaunchKernelGGL((decode_merge_kernel<E, D, PAGED>), dim3(B * a.H), dim3(D < 256 ? D : 256), 0, stream, a);
   return hipGetLastError();
+}
+
+template <typename E, int D, int G>
+static hipError_t launch_decode_t(DecodeArgs a, int B, int KVH, hipStream_t stream) {
+  return a.table ? launch_decode_p<E, D, G, true>(a, B, KVH, stream)
+                 : launch_decode_p<E, D, G, false>(a, B, KVH, stream);
 }
 
 template <typename E>
@@ -307,7 +360,12 @@ hipError_t launch_decode(const DecodeLaunch& L, int dtype, hipStream_t stream) {
   a.cap = make_cap_consts(L.query_scale, L.softcap);
   a.window = L.window;
   a.is_local = L.is_local;
-  a.nsplit = decode_splits(L.S);
+  a.nsplit = decode_call_splits(L);
+  a.table = L.block_table;
+  a.max_blocks = L.max_blocks;
+  a.num_blocks = L.num_blocks;
+  a.bs_log2 = 0;
+  while (L.block_size > (1 << a.bs_log2)) ++a.bs_log2;
   const size_t n = (size_t)L.B * L.H * a.nsplit;
   float* ws = static_cast<float*>(L.workspace);
   a.ws_m = ws;

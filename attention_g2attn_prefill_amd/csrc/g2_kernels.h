@@ -27,6 +27,10 @@ struct DecodeLaunch {
   float query_scale, softcap;
   int window, is_local;
   void* workspace;
+  // Paged mode when block_table is non-null: k/v are (num_blocks,
+  // block_size, KVH, d) pools and S is unused.
+  const int32_t* block_table = nullptr;
+  int max_blocks = 0, block_size = 0, num_blocks = 0;
 };
 
 // Keys handled by one split-K workgroup of the decode kernel.
@@ -38,6 +42,15 @@ inline int decode_splits(int S) { return (S + kDecodeChunk - 1) / kDecodeChunk; 
 inline size_t decode_workspace_bytes(int B, int H, int d, int S) {
   const size_t n = (size_t)B * H * decode_splits(S);
   return n * (2 + (size_t)d) * sizeof(float);
+}
+
+// Splits of a decode call: enough 512-position chunks for the most positions
+// one query can see.
+inline int decode_call_splits(const DecodeLaunch& L) {
+  if (!L.block_table) return decode_splits(L.S);
+  const long long cap = (long long)L.max_blocks * L.block_size;
+  const long long seen = L.is_local && L.window < cap ? L.window : cap;
+  return (int)((seen + kDecodeChunk - 1) / kDecodeChunk);
 }
 
 hipError_t launch_prefill_bf16(const PrefillLaunch& L, hipStream_t stream);

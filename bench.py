@@ -5,7 +5,9 @@ One step = the whole hot path on seeded synthetic inputs shaped like Gemma 2 9B:
   prefill of a local (sliding window 4096) and a global layer at B=2, T=S=8192,
   H=16, KVH=8, d=256, softcap 50, query_scale 1/16; then decode of one token
   for 64 sequences against a global linear cache (L_b uniform on [4096, 8192])
-  and a local 4096-slot ring.
+  and a local 4096-slot ring; then the same decode against a paged cache
+  (16-token blocks at seeded random pool positions, one block table per
+  sequence).
 
 Reported (one JSON line):
   value    prefill effective TFLOP/s = algorithmic FLOPs of the pair / prefill
@@ -237,6 +239,20 @@ def main():
     DB, DS, DH, DKVH, Dd = dq.shape[0], kgd.shape[1], dq.shape[2], kgd.shape[2], dq.shape[3]
     W = cfg_p["window"]
     ws = torch.empty(g2.decode_workspace_bytes(DB, DH, Dd, DS), dtype=torch.uint8, device=dev)
+    # paged cache: the global cache's 16-token blocks scattered over a pool
+    PBS = 16
+    maxb = DS // PBS
+    gen = torch.Generator().manual_seed(16)
+    perm = torch.randperm(DB * maxb, generator=gen).to(dev)
+    kpool = torch.empty((DB * maxb, PBS, DKVH, Dd), dtype=kgd.dtype, device=dev)
+    vpool = torch.empty_like(kpool)
+    kpool[perm] = kgd.view(DB * maxb, PBS, DKVH, Dd)
+    vpool[perm] = vgd.view(DB * maxb, PBS, DKVH, Dd)
+    table = perm.view(DB, maxb).to(torch.int32).contiguous()
+    pout_l = torch.empty_like(dqd)
+    pout_g = torch.empty_like(dqd)
+    pws = torch.empty(g2.decode_paged_workspace_bytes(DB, DH, Dd, maxb, PBS), dtype=torch.uint8,
+                      device=dev)
     torch.cuda.synchronize()
 
     kw_p = dict(query_scale=cfg_p["query_scale"], softcap=cfg_p["softcap"], window=W)
@@ -261,12 +277,20 @@ def main():
                   stream=stream, **kw_d)
         if ev is not None:
             ev[4].record(stream)
+        g2.decode_paged(dqd, kpool, vpool, table, lens_d, is_local=True, out=pout_l,
+                        workspace=pws, stream=stream, **kw_d)
+        if ev is not None:
+            ev[5].record(stream)
+        g2.decode_paged(dqd, kpool, vpool, table, lens_d, is_local=False, out=pout_g,
+                        workspace=pws, stream=stream, **kw_d)
+        if ev is not None:
+            ev[6].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -275,9 +299,9 @@ def main():
     wall = time.perf_counter() - t0
     print(f"[bench] timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
 
-    ms = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(4)]
-                   for i in range(args.steps)])  # per step: pl, pg, dl, dg (ms)
-    t_pl, t_pg, t_dl, t_dg = ms.mean(axis=0) * 1e-3
+    ms = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(6)]
+                   for i in range(args.steps)])  # per step: pl, pg, dl, dg, paged l, paged g (ms)
+    t_pl, t_pg, t_dl, t_dg, t_ql, t_qg = ms.mean(axis=0) * 1e-3
     med = np.median(ms, axis=0)
     mn = ms.min(axis=0)
 
@@ -305,6 +329,7 @@ def main():
     b_local = float(n_local * row_bytes + qo_bytes)
     b_global = float(n_global * row_bytes + qo_bytes)
     decode_gbs = (b_local + b_global) / (t_dl + t_dg) / 1e9
+    paged_gbs = (b_local + b_global) / (t_ql + t_qg) / 1e9
 
     src_hash = kernel_source_hash()
     traffic = measured_traffic(src_hash)
@@ -322,6 +347,14 @@ def main():
               "ms_global_median_min": [round(med[3], 4), round(mn[3], 4)],
               "bytes_local": b_local, "bytes_global": b_global,
               "device_copy_gbs_context": round(copy_rate, 1)}
+    decode_paged = {"metric": "paged decode KV GB/s", "value": round(paged_gbs, 1), "unit": "GB/s",
+                    "block_size": PBS,
+                    "roofline": {"bound": "hbm", "achieved": round(paged_gbs, 1),
+                                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                 "frac": round(paged_gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                    "ms_local": round(t_ql * 1e3, 4), "ms_global": round(t_qg * 1e3, 4),
+                    "ms_local_median_min": [round(med[4], 4), round(mn[4], 4)],
+                    "ms_global_median_min": [round(med[5], 4), round(mn[5], 4)]}
     per_layer = {"prefill_local_ms": round(t_pl * 1e3, 4), "prefill_global_ms": round(t_pg * 1e3, 4),
                  "prefill_local_tflops": round(f_local / t_pl / 1e12, 2),
                  "prefill_global_tflops": round(f_global / t_pg / 1e12, 2),
@@ -356,6 +389,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "decode": decode,
+        "decode_paged": decode_paged,
         "per_layer": per_layer,
         "kernel_source_sha256": src_hash[:16],
     }

@@ -111,6 +111,49 @@ int g2attn_decode(const void* q, const void* k_cache, const void* v_cache,
 size_t g2attn_decode_workspace_bytes(int B, int H, int d, int S);
 
 /*
+ * Decode against a paged KV cache (Gemma 2 Guide, "Deep Dive" item 2: serving
+ * runtimes keep KV memory in fixed-size blocks, and local layers drop the
+ * blocks older than the window).
+ *   q, out          : (B, 1, H, d)
+ *   k_pool, v_pool  : (num_blocks, block_size, KVH, d), the caller's block pool.
+ *   block_table     : device int32[B * max_blocks]; entry [b][i] is the pool
+ *                     block holding positions i*block_size .. (i+1)*block_size-1
+ *                     of sequence b.  Only entries of blocks that hold a
+ *                     position the query sees are read, so entries of unused
+ *                     or dropped blocks may hold anything (e.g. -1).
+ *   kv_lens         : device int32[B]; L_b tokens, the newest (already
+ *                     written) at position L_b - 1, the query's position;
+ *                     1 <= L_b <= max_blocks * block_size.  The visible
+ *                     positions are those the prefill mask allows.
+ *   block_size      : a power of two, 1 .. 65536.
+ *   workspace       : device scratch of at least
+ *                     g2attn_decode_paged_workspace_bytes(B, H, d, max_blocks,
+ *                     block_size) bytes; owned by the caller.
+ * A sequence whose L_b is out of range, or whose visible positions need a
+ * table entry outside [0, num_blocks), gets NaN outputs; nothing outside the
+ * pool is read.  Other errors as for g2attn_decode.
+ */
+int g2attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
+                        void* out, const int32_t* block_table, int max_blocks,
+                        const int32_t* kv_lens, int B, int H, int KVH, int d,
+                        int block_size, int num_blocks, float query_scale,
+                        float softcap, int window, int is_local, int dtype,
+                        void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/* Bytes of paged-decode workspace for these sizes (0 for invalid sizes). */
+size_t g2attn_decode_paged_workspace_bytes(int B, int H, int d, int max_blocks,
+                                           int block_size);
+
+/*
+ * Host-only validation of the scalar arguments of g2attn_decode_paged,
+ * returning the status the call would return for non-null, aligned pointers.
+ */
+int g2attn_check_paged_args(int B, int H, int KVH, int d, int block_size,
+                            int max_blocks, int num_blocks, int window,
+                            int is_local, int dtype);
+
+/*
  * Host-only validation of the scalar arguments of either entry point
  * (decode = 1 for decode), returning the status the call would return for
  * non-null, aligned pointers.  Touches no GPU.

@@ -23,7 +23,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("g2attn_prefill", "g2attn_decode", "g2attn_decode_workspace_bytes",
-              "g2attn_check_args", "g2attn_status_string"):
+              "g2attn_check_args", "g2attn_status_string", "g2attn_decode_paged",
+              "g2attn_decode_paged_workspace_bytes", "g2attn_check_paged_args"):
         assert n in names
 
 
@@ -100,3 +101,47 @@ def test_binding_requires_gpu_tensors():
     k = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(TypeError):
         g2.prefill(q, k, k, query_scale=0.125, is_local=False)
+
+
+@pytest.mark.parametrize("args,expect", [
+    # B, H, KVH, d, block_size, max_blocks, num_blocks, window, is_local, dtype
+    ((64, 16, 8, 256, 16, 512, 32768, 4096, 1, 0), OK),
+    ((2, 4, 2, 64, 1, 100, 7, 5, 0, 1), OK),
+    ((2, 4, 2, 64, 65536, 2, 7, 5, 0, 0), OK),
+    ((2, 4, 2, 64, 24, 10, 7, 5, 0, 0), ARG),          # block size not a power of two
+    ((2, 4, 2, 64, 0, 10, 7, 5, 0, 0), ARG),
+    ((2, 4, 2, 64, 131072, 10, 7, 5, 0, 0), ARG),     # block size above 65536
+    ((2, 4, 2, 64, 16, 0, 7, 5, 0, 0), ARG),
+    ((2, 4, 2, 64, 16, 10, 0, 5, 0, 0), ARG),
+    ((2, 4, 2, 64, 65536, 1 << 15, 7, 5, 0, 0), ARG),  # capacity beyond 2^31 positions
+    ((2, 4, 2, 64, 16, 10, 7, 0, 1, 0), ARG),          # local with window 0
+    ((2, 4, 3, 64, 16, 10, 7, 5, 0, 0), ARG),          # H % KVH
+    ((2, 4, 2, 96, 16, 10, 7, 5, 0, 0), UNSUP),
+    ((2, 8, 2, 64, 16, 10, 7, 5, 0, 0), UNSUP),
+])
+def test_check_paged_args(args, expect):
+    assert g2.check_paged_args(*args) == expect
+
+
+def test_paged_workspace_bytes():
+    # splits of 512 positions over the table's capacity max_blocks * block_size
+    assert g2.decode_paged_workspace_bytes(64, 16, 256, 512, 16) == 64 * 16 * 16 * 258 * 4
+    assert g2.decode_paged_workspace_bytes(1, 1, 64, 3, 1) == 66 * 4
+    assert g2.decode_paged_workspace_bytes(1, 1, 64, 0, 16) == 0
+
+
+def test_paged_entry_point_rejects_before_launching():
+    lib = g2.lib
+    a = _fake(0x10000)
+    null = ctypes.c_void_p(0)
+    need = g2.decode_paged_workspace_bytes(2, 4, 64, 8, 16)
+    args = lambda q=a, kp=a, vp=a, out=a, tab=a, lens=a, ws=a, nbytes=need, bs=16: (
+        q, kp, vp, out, tab, 8, lens, 2, 4, 2, 64, bs, 10, 1.0, 50.0, 64, 1, 0, ws, nbytes, null)
+    assert lib.g2attn_decode_paged(*args(bs=12)) == ARG
+    assert lib.g2attn_decode_paged(*args(tab=null)) == ARG
+    assert lib.g2attn_decode_paged(*args(lens=null)) == ARG
+    assert lib.g2attn_decode_paged(*args(kp=_fake(0x10004))) == ALIGN
+    assert lib.g2attn_decode_paged(*args(ws=null)) == WS
+    # a local layer needs only the splits of its window: 64 positions here
+    small = g2.decode_paged_workspace_bytes(2, 4, 64, 1, 64)
+    assert lib.g2attn_decode_paged(*args(nbytes=small - 1)) == WS
