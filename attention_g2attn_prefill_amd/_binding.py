@@ -26,6 +26,9 @@ _F = ctypes.c_float
 lib.g2attn_prefill.argtypes = [_vp, _vp, _vp, _vp, _I, _I, _I, _I, _I, _I, _F, _F, _I, _I,
                                _I, _vp]
 lib.g2attn_prefill.restype = _I
+lib.g2attn_prefill_lse.argtypes = [_vp, _vp, _vp, _vp, _vp, _I, _I, _I, _I, _I, _I, _F, _F,
+                                   _I, _I, _I, _vp]
+lib.g2attn_prefill_lse.restype = _I
 lib.g2attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _I, _I, _I, _I, _I, _I, _F, _F, _I,
                               _I, _I, _vp, ctypes.c_size_t, _vp]
 lib.g2attn_decode.restype = _I
@@ -116,6 +119,33 @@ def prefill(q, k, v, *, query_scale, softcap=50.0, window=4096, is_local, out=No
     if st != 0:
         raise G2attnError(st, "g2attn_prefill")
     return out
+
+
+def prefill_lse(q, k, v, *, query_scale, softcap=50.0, window=4096, is_local, out=None,
+                lse=None, stream=None):
+    """prefill() that also returns the (B, H, T) float32 natural-log log-sum-exp
+    of each row's capped, masked logits.  Returns (out, lse)."""
+    B, T, H, d = q.shape
+    Bk, S, KVH, dk = k.shape
+    if (Bk, dk) != (B, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch: q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share dtype bfloat16 or float32")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q's shape and dtype")
+    if lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    elif tuple(lse.shape) != (B, H, T) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 of shape (B, H, T)")
+    st = lib.g2attn_prefill_lse(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+                                _dev(lse, "lse"), B, T, S, H, KVH, d, float(query_scale),
+                                float(softcap), int(window), int(bool(is_local)),
+                                _DTYPES[q.dtype], _stream_handle(stream))
+    if st != 0:
+        raise G2attnError(st, "g2attn_prefill_lse")
+    return out, lse
 
 
 def decode(q, k_cache, v_cache, kv_lens, *, query_scale, softcap=50.0, window=4096,

@@ -90,6 +90,21 @@ int g2attn_prefill(const void* q, const void* k, const void* v, void* out, int B
   return e == hipSuccess ? G2_OK : G2_ERR_LAUNCH;
 }
 
+int g2attn_prefill_lse(const void* q, const void* k, const void* v, void* out, float* lse,
+                       int B, int T, int S, int H, int KVH, int d, float query_scale,
+                       float softcap, int window, int is_local, int dtype, hipStream_t stream) {
+  int st = check_scalars(B, T, S, H, KVH, d, window, is_local, dtype, 0);
+  if (st != G2_OK) return st;
+  if (!q || !k || !v || !out || !lse) return G2_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return G2_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return G2_ERR_ALIGN;
+  g2::PrefillLaunch L{q, k, v, out, B, T, S, H, KVH, d, query_scale, softcap, window, is_local};
+  L.lse = lse;
+  const hipError_t e = dtype == G2_BF16 ? g2::launch_prefill_bf16(L, stream)
+                                        : g2::launch_prefill_f32(L, stream);
+  return e == hipSuccess ? G2_OK : G2_ERR_LAUNCH;
+}
+
 int g2attn_decode(const void* q, const void* k_cache, const void* v_cache, void* out,
                   const int32_t* kv_lens, int B, int T, int S, int H, int KVH, int d,
                   float query_scale, float softcap, int window, int is_local, int dtype,

@@ -15,6 +15,7 @@ struct PrefillLaunch {
   int B, T, S, H, KVH, d;
   float query_scale, softcap;
   int window, is_local;
+  float* lse = nullptr;  // optional (B, H, T) natural-log log-sum-exp of each row
 };
 
 struct DecodeLaunch {

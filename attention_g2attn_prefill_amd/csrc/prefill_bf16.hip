@@ -76,6 +76,7 @@ struct PrefillArgs {
   const bf16* k;
   const bf16* v;
   bf16* out;
+  float* lse;  // optional (B, H, T), natural log
   int T, S, H, KVH;
   CapConsts cap;
   int window;
@@ -372,6 +373,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
     const float lt = sum_xor16_32(l_run[qb]);
     const float inv = 1.0f / lt;
     const int t = t0 + qb * 16 + l16;
+    // l and O are kept relative to 2^m_run (log2 units of the capped logit)
+    if (a.lse && lq == 0 && t < T)
+      a.lse[((size_t)b * H + h) * T + t] = (m_run[qb] + __log2f(lt)) * 0.69314718055994531f;
     if (t < T) {
       bf16* orow = a.out + (((size_t)b * T + t) * H + h) * D + lq * 4;
 #pragma unroll
@@ -410,6 +414,7 @@ hipError_t launch_prefill_bf16(const PrefillLaunch& L, hipStream_t stream) {
   a.k = static_cast<const bf16*>(L.k);
   a.v = static_cast<const bf16*>(L.v);
   a.out = static_cast<bf16*>(L.out);
+  a.lse = L.lse;
   a.T = L.T;
   a.S = L.S;
   a.H = L.H;

@@ -16,6 +16,7 @@ struct PrefillF32Args {
   const float* k;
   const float* v;
   float* out;
+  float* lse;  // optional (B, H, T), natural log
   int B, T, S, H, KVH, G;
   float query_scale, softcap;
   int use_cap, window, is_local;
@@ -71,6 +72,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillF32Args a) {
   float* orow = a.out + row * D;
 #pragma unroll
   for (int e = 0; e < E; ++e) orow[lane + 64 * e] = acc[e] / l;
+  if (a.lse && lane == 0) a.lse[((size_t)b * a.H + h) * a.T + t] = m + logf(l);
 }
 
 hipError_t launch_prefill_f32(const PrefillLaunch& L, hipStream_t stream) {
@@ -79,6 +81,7 @@ hipError_t launch_prefill_f32(const PrefillLaunch& L, hipStream_t stream) {
   a.k = static_cast<const float*>(L.k);
   a.v = static_cast<const float*>(L.v);
   a.out = static_cast<float*>(L.out);
+  a.lse = L.lse;
   a.B = L.B;
   a.T = L.T;
   a.S = L.S;

@@ -7,7 +7,8 @@ One step = the whole hot path on seeded synthetic inputs shaped like Gemma 2 9B:
   for 64 sequences against a global linear cache (L_b uniform on [4096, 8192])
   and a local 4096-slot ring; then the same decode against a paged cache
   (16-token blocks at seeded random pool positions, one block table per
-  sequence).
+  sequence); and a chunked prefill: the last 2048 queries of the 9B batch
+  against its whole 8192-token cache (local and global).
 
 Reported (one JSON line):
   value    prefill effective TFLOP/s = algorithmic FLOPs of the pair / prefill
@@ -249,6 +250,10 @@ def main():
     kpool[perm] = kgd.view(DB * maxb, PBS, DKVH, Dd)
     vpool[perm] = vgd.view(DB * maxb, PBS, DKVH, Dd)
     table = perm.view(DB, maxb).to(torch.int32).contiguous()
+    CT = 2048
+    qchunk = qd[:, T - CT:].contiguous() if T > CT else qd
+    CT = qchunk.shape[1]
+    cout = torch.empty_like(qchunk)
     pout_l = torch.empty_like(dqd)
     pout_g = torch.empty_like(dqd)
     pws = torch.empty(g2.decode_paged_workspace_bytes(DB, DH, Dd, maxb, PBS), dtype=torch.uint8,
@@ -285,12 +290,18 @@ def main():
                         workspace=pws, stream=stream, **kw_d)
         if ev is not None:
             ev[6].record(stream)
+        g2.prefill(qchunk, kd, vd, is_local=True, out=cout, stream=stream, **kw_p)
+        if ev is not None:
+            ev[7].record(stream)
+        g2.prefill(qchunk, kd, vd, is_local=False, out=cout, stream=stream, **kw_p)
+        if ev is not None:
+            ev[8].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(9)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -299,9 +310,9 @@ def main():
     wall = time.perf_counter() - t0
     print(f"[bench] timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
 
-    ms = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(6)]
-                   for i in range(args.steps)])  # per step: pl, pg, dl, dg, paged l, paged g (ms)
-    t_pl, t_pg, t_dl, t_dg, t_ql, t_qg = ms.mean(axis=0) * 1e-3
+    ms = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(8)]
+                   for i in range(args.steps)])  # pl, pg, dl, dg, paged l, paged g, chunk l, chunk g
+    t_pl, t_pg, t_dl, t_dg, t_ql, t_qg, t_cl, t_cg = ms.mean(axis=0) * 1e-3
     med = np.median(ms, axis=0)
     mn = ms.min(axis=0)
 
@@ -330,6 +341,9 @@ def main():
     b_global = float(n_global * row_bytes + qo_bytes)
     decode_gbs = (b_local + b_global) / (t_dl + t_dg) / 1e9
     paged_gbs = (b_local + b_global) / (t_ql + t_qg) / 1e9
+    fc_local = 4.0 * d * B * H * prefill_pairs(CT, S, W, True)
+    fc_global = 4.0 * d * B * H * prefill_pairs(CT, S, W, False)
+    chunk_tflops = (fc_local + fc_global) / (t_cl + t_cg) / 1e12
 
     src_hash = kernel_source_hash()
     traffic = measured_traffic(src_hash)
@@ -390,6 +404,11 @@ def main():
         "cpu_baseline": cpu,
         "decode": decode,
         "decode_paged": decode_paged,
+        "prefill_chunk": {"metric": "chunked prefill eff. TFLOP/s", "value": round(chunk_tflops, 2),
+                          "unit": "TFLOP/s", "chunk": CT, "cache": S,
+                          "frac_of_bf16_peak": round(chunk_tflops / PEAK_BF16_TFLOPS, 4),
+                          "ms_local": round(t_cl * 1e3, 4), "ms_global": round(t_cg * 1e3, 4),
+                          "flops_local": fc_local, "flops_global": fc_global},
         "per_layer": per_layer,
         "kernel_source_sha256": src_hash[:16],
     }

@@ -80,6 +80,19 @@ int g2attn_prefill(const void* q, const void* k, const void* v, void* out,
                    int dtype, hipStream_t stream);
 
 /*
+ * Prefill that also returns each row's log-sum-exp, the statistic a backward
+ * pass keeps from the forward (Gemma 2 Guide, "Deep Dive" item 1: the cap is
+ * differentiated in training).  Arguments as for g2attn_prefill, plus
+ *   lse : device float32 (B, H, T), 4-byte aligned; lse[b][h][t] is the
+ *         natural-log log-sum-exp over the visible keys of the capped logits
+ *         s_j of row (b, t, h), so the softmax weights are exp(s_j - lse).
+ */
+int g2attn_prefill_lse(const void* q, const void* k, const void* v, void* out,
+                       float* lse, int B, int T, int S, int H, int KVH, int d,
+                       float query_scale, float softcap, int window,
+                       int is_local, int dtype, hipStream_t stream);
+
+/*
  * Decode: one new query token per sequence against a KV cache of capacity S
  * (model card, "Method"; Guide section 2 on local layers keeping only the last
  * 4096 tokens).

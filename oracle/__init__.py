@@ -54,6 +54,9 @@ def _load():
                                      _I, _I, _I, _I, _I, _D, _D, _I, _I, _i64p,
                                      ctypes.c_int64]
     lib.g2o_decode_paged.restype = _I
+    lib.g2o_prefill_lse.argtypes = [_f32p, _f32p, _f64p, _I, _I, _I, _I, _I, _I, _D, _D,
+                                    _I, _I, _i64p, ctypes.c_int64]
+    lib.g2o_prefill_lse.restype = _I
     lib.g2o_threads.argtypes = []
     lib.g2o_threads.restype = _I
     _lib = lib
@@ -222,6 +225,32 @@ def decode_paged(q, k_pool, v_pool, block_table, kv_lens, *, query_scale, softca
                                   _ptr(table, _i32p), table.shape[1], _ptr(lens, _i32p),
                                   _ptr(out, _f64p), B, H, KVH, d, BS, NB, query_scale,
                                   softcap, window, int(bool(is_local)), rp, n)
+    if st != 0:
+        raise OracleError(f"oracle rejected arguments (status {st})")
+    return out
+
+
+def prefill_lse(q, k, *, query_scale, softcap, window, is_local, rows=None):
+    """Natural-log log-sum-exp of each prefill row's capped, masked logits.
+
+    q: (B,T,H,d); k: (B,S,KVH,d).  rows=None returns (B,T,H); otherwise rows
+    are flat ids (b*T + t)*H + h and the result has one entry per row.
+    """
+    q, k = _f32(q), _f32(k)
+    B, T, H, d = q.shape
+    S, KVH = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != d:
+        raise OracleError("shape mismatch")
+    if rows is None:
+        out = np.empty((B, T, H), np.float64)
+        rp, n = None, 0
+    else:
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        out = np.empty(rows.size, np.float64)
+        rp, n = _ptr(rows, _i64p), rows.size
+    st = _load().g2o_prefill_lse(_ptr(q, _f32p), _ptr(k, _f32p), _ptr(out, _f64p), B, T, S, H,
+                                 KVH, d, query_scale, softcap, window, int(bool(is_local)),
+                                 rp, n)
     if st != 0:
         raise OracleError(f"oracle rejected arguments (status {st})")
     return out

@@ -209,6 +209,51 @@ int g2o_prefill(const float* q, const float* k, const float* v, double* out,
   return G2O_OK;
 }
 
+/* Log-sum-exp of the capped, masked logits of prefill rows (natural log):
+ * lse = log sum_j exp(s_j) over the keys row (b, t, h) sees.  It is what a
+ * backward pass saves from the forward (Gemma 2 Guide, "Deep Dive" item 1
+ * differentiates the cap; the softmax weights are exp(s_j - lse)).
+ * rows == NULL: every row, lse is (B,T,H); else rows r = (b*T + t)*H + h. */
+int g2o_prefill_lse(const float* q, const float* k, double* lse, int B, int T,
+                    int S, int H, int KVH, int d, double query_scale,
+                    double softcap, int window, int is_local,
+                    const int64_t* rows, int64_t nrows) {
+  if (!check_shapes(B, T, S, H, KVH, d, window, is_local)) return G2O_ERR_ARG;
+  const int64_t total = (int64_t)B * T * H;
+  const int64_t n = rows ? nrows : total;
+  if (rows) {
+    for (int64_t i = 0; i < n; ++i)
+      if (rows[i] < 0 || rows[i] >= total) return G2O_ERR_ARG;
+  }
+#pragma omp parallel
+  {
+    const float** k_rows = (const float**)malloc(sizeof(float*) * (size_t)S);
+    unsigned char* allowed = (unsigned char*)malloc((size_t)S);
+    double* s = (double*)malloc(sizeof(double) * (size_t)S);
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t i = 0; i < n; ++i) {
+      const int64_t r = rows ? rows[i] : i;
+      const int h = (int)(r % H);
+      const int t = (int)((r / H) % T);
+      const int b = (int)(r / ((int64_t)H * T));
+      prefill_row_setup(k, T, S, H, KVH, d, window, is_local, b, t, h, k_rows,
+                        allowed);
+      row_logits(q + r * d, k_rows, allowed, S, d, query_scale, softcap, s);
+      double m = -INFINITY;
+      for (int64_t j = 0; j < S; ++j)
+        if (s[j] > m) m = s[j];
+      double z = 0.0;
+      for (int64_t j = 0; j < S; ++j)
+        if (s[j] != -INFINITY) z += exp(s[j] - m);
+      lse[i] = m + log(z);
+    }
+    free(k_rows);
+    free(allowed);
+    free(s);
+  }
+  return G2O_OK;
+}
+
 /* Decode of one new token per sequence against a KV cache.
  * q,out: (B,1,H,d); k_cache, v_cache: (B,S,KVH,d); kv_lens[b] = L_b >= 1 is
  * the number of tokens the sequence holds, the newest one (already written)

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("g2attn_prefill", "g2attn_decode", "g2attn_decode_workspace_bytes",
+    for n in ("g2attn_prefill", "g2attn_prefill_lse", "g2attn_decode", "g2attn_decode_workspace_bytes",
               "g2attn_check_args", "g2attn_status_string", "g2attn_decode_paged",
               "g2attn_decode_paged_workspace_bytes", "g2attn_check_paged_args"):
         assert n in names

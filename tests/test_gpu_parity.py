@@ -154,6 +154,100 @@ def test_prefill_full_size_sampled(g2, name, is_local, prefill_inputs_cache):
     check(got, ref, cfg["dtype"], f"{name} {'local' if is_local else 'global'} ({rows.size} rows)")
 
 
+# --------------------------------------------------- log-sum-exp of each row
+
+LSE_BF16_MAX, LSE_F32_MAX = 2e-3, 1e-4
+
+LSE_CASES = [
+    # B, T, S, H, KVH, d, window, is_local, dtype, q_mul
+    (2, 300, 300, 4, 2, 256, 64, True, "bf16", 3.0),
+    (2, 300, 300, 4, 2, 256, 64, False, "bf16", 3.0),
+    (1, 100, 330, 4, 2, 128, 70, True, "bf16", 5.5),       # T < S, saturating logits
+    (1, 200, 200, 2, 2, 64, 33, False, "bf16", 2.0),
+    (1, 256, 256, 4, 2, 64, 64, True, "f32", 4.0),
+    (1, 129, 257, 2, 1, 256, 100, False, "f32", 2.0),
+]
+
+
+@pytest.mark.parametrize("case", LSE_CASES, ids=[f"lse{i}" for i in range(len(LSE_CASES))])
+def test_prefill_lse(g2, case):
+    B, T, S, H, KVH, d, W, is_local, dt, qm = case
+    say(f"prefill lse {case}")
+    seed = 600 + d + T
+    q = synth.draw((B, T, H, d), seed, 0, dtype=dt, mul=qm)
+    k = synth.draw((B, S, KVH, d), seed, 1, dtype=dt, mul=qm if qm > 4 else 1.0)
+    v = synth.draw((B, S, KVH, d), seed, 2, dtype=dt)
+    kw = dict(query_scale=1 / np.sqrt(d), softcap=50.0, window=W, is_local=is_local)
+    out, lse = g2.prefill_lse(q.cuda(), k.cuda(), v.cuda(), **kw)
+    plain = g2.prefill(q.cuda(), k.cuda(), v.cuda(), **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out, plain)          # the extra output changes nothing else
+    qn, kn = synth.to_f32_numpy(q), synth.to_f32_numpy(k)
+    ref = oracle.prefill_lse(qn, kn, **kw).transpose(0, 2, 1)     # (B, H, T)
+    err = np.abs(lse.cpu().numpy().astype(np.float64) - ref)
+    say(f"lse {case}: max|d|={err.max():.3e}")
+    assert np.all(np.isfinite(err)) and err.max() <= (LSE_F32_MAX if dt == "f32" else LSE_BF16_MAX)
+
+
+@pytest.mark.parametrize("is_local", [True, False], ids=["local", "global"])
+def test_prefill_lse_full_size_sampled(g2, is_local, prefill_inputs_cache):
+    name = "9b-8k"
+    cfg = synth.WORKLOADS[name]
+    say(f"prefill lse full {name} {'local' if is_local else 'global'}")
+    if name not in prefill_inputs_cache:
+        prefill_inputs_cache.clear()
+        q, k, v = synth.prefill_inputs(cfg)
+        prefill_inputs_cache[name] = (q, k, v, q.cuda(), k.cuda(), v.cuda(),
+                                      synth.to_f32_numpy(k), synth.to_f32_numpy(v))
+    q, k, v, qd, kd, vd, kn, vn = prefill_inputs_cache[name]
+    kw = layer_kw(cfg, is_local)
+    _, lse = g2.prefill_lse(qd, kd, vd, **kw)
+    torch.cuda.synchronize()
+    B, T, H, d = q.shape
+    rows = sample_rows(B, T, H, cfg["window"], seed=cfg["seed"] + 1, n_random=60)
+    ref = oracle.prefill_lse(synth.to_f32_numpy(q), kn, rows=rows, **kw)
+    b, t, h = rows // (T * H), (rows // H) % T, rows % H
+    got = lse.cpu().numpy()[b, h, t].astype(np.float64)
+    err = np.abs(got - ref)
+    say(f"lse full: max|d|={err.max():.3e} over {rows.size} rows")
+    assert np.all(np.isfinite(got)) and err.max() <= LSE_BF16_MAX
+
+
+# ---------------------------------------------- chunked prefill (T < S)
+
+@pytest.mark.parametrize("T", [2048, 1000])
+@pytest.mark.parametrize("is_local", [True, False], ids=["local", "global"])
+def test_chunked_prefill_9b(g2, T, is_local, prefill_inputs_cache):
+    """The last T queries against the whole 8192-token cache: rows sit at
+    positions t + S - T.  They equal the last T rows of the full prefill
+    (bit for bit when the chunk starts on a 64-row boundary) and the oracle
+    on sampled rows."""
+    name = "9b-8k"
+    cfg = synth.WORKLOADS[name]
+    say(f"chunked prefill T={T} {'local' if is_local else 'global'}")
+    if name not in prefill_inputs_cache:
+        prefill_inputs_cache.clear()
+        q, k, v = synth.prefill_inputs(cfg)
+        prefill_inputs_cache[name] = (q, k, v, q.cuda(), k.cuda(), v.cuda(),
+                                      synth.to_f32_numpy(k), synth.to_f32_numpy(v))
+    q, k, v, qd, kd, vd, kn, vn = prefill_inputs_cache[name]
+    kw = layer_kw(cfg, is_local)
+    S = k.shape[1]
+    full = g2.prefill(qd, kd, vd, **kw)
+    chunk = g2.prefill(qd[:, S - T:].contiguous(), kd, vd, **kw)
+    torch.cuda.synchronize()
+    tail = full[:, S - T:]
+    if (S - T) % 64 == 0:
+        assert torch.equal(chunk, tail)
+    else:
+        assert float((chunk.float() - tail.float()).abs().max()) <= 1e-2
+    B, _, H, d = q.shape
+    rows = sample_rows(B, T, H, cfg["window"], seed=T, n_random=60)
+    ref = oracle.prefill(synth.to_f32_numpy(q[:, S - T:]), kn, vn, rows=rows, **kw)
+    got = synth.to_f32_numpy(chunk).reshape(-1, d)[rows]
+    check(got, ref, "bf16", f"chunk T={T} {'local' if is_local else 'global'} ({rows.size} rows)")
+
+
 # -------------------------------------------------------------- invariants
 
 def test_window_at_least_T_equals_global_bitwise(g2):

@@ -539,3 +539,49 @@ def test_decode_paged_rejects_bad_lengths():
         with pytest.raises(oracle.OracleError):
             oracle.decode_paged(q.numpy(), kp.numpy(), kp.numpy(), tab, np.array(bad, np.int32),
                                 query_scale=1.0, softcap=50.0, window=4, is_local=True)
+
+
+# ---- log-sum-exp of prefill rows (what a backward pass saves from the forward)
+
+@pytest.mark.parametrize("is_local", [False, True])
+def test_prefill_lse_matches_mpmath(is_local):
+    B, T, S, H, KVH, d, W = 1, 9, 12, 4, 2, 6, 4
+    q, k = rand((B, T, H, d), 241, mul=4.0), rand((B, S, KVH, d), 242)
+    qs = mpmath.mpf(0.7)
+    got = oracle.prefill_lse(q, k, query_scale=0.7, softcap=5.0, window=W, is_local=is_local)
+    for t in range(T):
+        for h in range(H):
+            s = [x for x in _mp_logits(q, k, 0, t, h, qs, mpmath.mpf(5), W, is_local, 2)
+                 if x is not None]
+            ref = mpmath.log(mpmath.fsum(mpmath.exp(x) for x in s))
+            assert abs(got[0, t, h] - float(ref)) <= 1e-13
+
+
+def test_prefill_lse_closed_forms():
+    B, T, S, H, KVH, d = 1, 30, 30, 2, 1, 8
+    k = rand((B, S, KVH, d), 251)
+    q0 = np.zeros((B, T, H, d), np.float32)
+    # zero query: every visible logit is 0, lse = log(number of visible keys)
+    glob = oracle.prefill_lse(q0, k, query_scale=1.0, softcap=50.0, window=7, is_local=False)
+    loc = oracle.prefill_lse(q0, k, query_scale=1.0, softcap=50.0, window=7, is_local=True)
+    t = np.arange(T)[None, :, None]
+    assert np.max(np.abs(glob - np.log(t + 1.0))) <= 1e-14
+    assert np.max(np.abs(loc - np.log(np.minimum(t + 1.0, 7.0)))) <= 1e-14
+    # window 1: the row sees only itself, lse = its own capped logit
+    q = rand((B, T, H, d), 252, mul=3.0)
+    one = oracle.prefill_lse(q, k, query_scale=0.5, softcap=4.0, window=1, is_local=True)
+    for tt in range(T):
+        x = float(np.dot(q[0, tt, 0].astype(np.float64) * 0.5, k[0, tt, 0].astype(np.float64)))
+        assert abs(one[0, tt, 0] - 4.0 * math.tanh(x / 4.0)) <= 1e-13
+
+
+def test_prefill_lse_normalises_the_weights():
+    """exp(s_j - lse) are the attention weights the (pinned) row routine gives."""
+    B, T, S, H, KVH, d = 1, 20, 20, 2, 1, 8
+    q, k = rand((B, T, H, d), 261, mul=3.0), rand((B, S, KVH, d), 262)
+    kw = dict(query_scale=0.5, softcap=50.0, window=6, is_local=True)
+    lse = oracle.prefill_lse(q, k, **kw)
+    for t in (0, 5, 19):
+        s = oracle.row_logits(q, k, 0, t, 1, **kw)
+        w = oracle.row_weights(q, k, 0, t, 1, **kw)
+        assert np.max(np.abs(np.exp(s - lse[0, t, 1]) - w)) <= 1e-14
