@@ -57,6 +57,10 @@ def _load():
     lib.g2o_prefill_lse.argtypes = [_f32p, _f32p, _f64p, _I, _I, _I, _I, _I, _I, _D, _D,
                                     _I, _I, _i64p, ctypes.c_int64]
     lib.g2o_prefill_lse.restype = _I
+    lib.g2o_rope.argtypes = [_f32p, _i32p, _f64p, _I, _I, _I, _I, _D]
+    lib.g2o_rope.restype = _I
+    lib.g2o_softcap_array.argtypes = [_f32p, _f64p, ctypes.c_int64, _D]
+    lib.g2o_softcap_array.restype = None
     lib.g2o_threads.argtypes = []
     lib.g2o_threads.restype = _I
     _lib = lib
@@ -253,4 +257,28 @@ def prefill_lse(q, k, *, query_scale, softcap, window, is_local, rows=None):
                                  rp, n)
     if st != 0:
         raise OracleError(f"oracle rejected arguments (status {st})")
+    return out
+
+
+def rope(x, positions, *, base=10000.0):
+    """Rotary embedding of x (B, T, NH, d) at positions (B, T), in float64.
+    Pair i is (x[..., i], x[..., i + d/2]), rotated by pos * base**(-2i/d)."""
+    x = _f32(x)
+    B, T, NH, d = x.shape
+    pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int32))
+    if pos.shape != (B, T):
+        raise OracleError("positions must be (B, T)")
+    out = np.empty(x.shape, np.float64)
+    st = _load().g2o_rope(_ptr(x, _f32p), _ptr(pos, _i32p), _ptr(out, _f64p), B, T, NH, d,
+                          float(base))
+    if st != 0:
+        raise OracleError(f"oracle rejected arguments (status {st})")
+    return out
+
+
+def softcap_array(x, cap):
+    """cap * tanh(x / cap) of every element, float64 (identity if cap <= 0 or inf)."""
+    x = _f32(x)
+    out = np.empty(x.shape, np.float64)
+    _load().g2o_softcap_array(_ptr(x, _f32p), _ptr(out, _f64p), x.size, float(cap))
     return out

@@ -395,6 +395,42 @@ int g2o_decode_paged(const float* q, const float* k_pool, const float* v_pool,
   return G2O_OK;
 }
 
+/* Rotary position embedding (wikillm model card, "Method" item 5: rotary
+ * embeddings carried over from Gemma 1; the pages give no formula).  Reading:
+ * the rotary embedding of Su et al. with pair i of a head vector formed by
+ * elements i and i + d/2 (i < d/2), rotated by the angle
+ * pos * base^(-2i/d):  (a, b) -> (a cos - b sin, b cos + a sin).
+ * x, out: (B, T, NH, d); positions: (B, T) int32.  d must be even. */
+int g2o_rope(const float* x, const int32_t* positions, double* out, int B,
+             int T, int NH, int d, double base) {
+  if (B <= 0 || T <= 0 || NH <= 0 || d <= 0 || (d & 1) || !(base > 1.0))
+    return G2O_ERR_ARG;
+  const int half = d / 2;
+  const int64_t rows = (int64_t)B * T;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    const double pos = (double)positions[r];
+    for (int i = 0; i < half; ++i) {
+      const double theta = pos * pow(base, -2.0 * i / d);
+      const double c = cos(theta), sn = sin(theta);
+      for (int h = 0; h < NH; ++h) {
+        const int64_t o = (r * NH + h) * d;
+        const double a = x[o + i], b = x[o + i + half];
+        out[o + i] = a * c - b * sn;
+        out[o + i + half] = b * c + a * sn;
+      }
+    }
+  }
+  return G2O_OK;
+}
+
+/* Final-logit soft-cap over an array (Guide section 1, second formula: the
+ * vocabulary logits are capped at 30 with the same tanh form). */
+void g2o_softcap_array(const float* x, double* out, int64_t n, double cap) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = g2o_softcap((double)x[i], cap);
+}
+
 /* Number of threads the parallel loops above use (OpenMP's default team). */
 #ifdef _OPENMP
 #include <omp.h>

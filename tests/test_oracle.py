@@ -585,3 +585,60 @@ def test_prefill_lse_normalises_the_weights():
         s = oracle.row_logits(q, k, 0, t, 1, **kw)
         w = oracle.row_weights(q, k, 0, t, 1, **kw)
         assert np.max(np.abs(np.exp(s - lse[0, t, 1]) - w)) <= 1e-14
+
+
+# ---- adjacent steps: rotary embedding and the final-logit cap
+
+def _rope_case(seed, B=2, T=9, NH=3, d=16, pmax=9000):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, T, NH, d)).astype(np.float32)
+    pos = rng.integers(0, pmax, size=(B, T)).astype(np.int32)
+    return x, pos
+
+
+def test_rope_position_zero_is_identity():
+    x, _ = _rope_case(271)
+    assert np.array_equal(oracle.rope(x, np.zeros(x.shape[:2], np.int32)), x.astype(np.float64))
+
+
+def test_rope_preserves_pair_norms():
+    x, pos = _rope_case(272)
+    y = oracle.rope(x, pos, base=10000.0)
+    h = x.shape[-1] // 2
+    nx = x[..., :h].astype(np.float64) ** 2 + x[..., h:].astype(np.float64) ** 2
+    ny = y[..., :h] ** 2 + y[..., h:] ** 2
+    assert np.max(np.abs(nx - ny)) <= 1e-12
+
+
+def test_rope_scores_depend_only_on_relative_position():
+    """<R(m) q, R(n) k> is unchanged when both positions shift by the same s."""
+    x, pos = _rope_case(273, B=1, T=2, NH=1, d=64, pmax=4000)
+    shifted = pos + 3171
+    a = oracle.rope(x, pos)
+    b = oracle.rope(x, shifted)
+    assert abs(float(a[0, 0, 0] @ a[0, 1, 0]) - float(b[0, 0, 0] @ b[0, 1, 0])) <= 1e-10
+    # and it does change with the distance
+    c = oracle.rope(x, np.array([[pos[0, 0], pos[0, 1] + 1]], np.int32))
+    assert abs(float(a[0, 0, 0] @ a[0, 1, 0]) - float(c[0, 0, 0] @ c[0, 1, 0])) > 1e-6
+
+
+def test_rope_frequency_schedule():
+    """A unit vector in pair i turns by pos * base**(-2i/d): pair 0 by pos
+    radians, pair d/4 by pos / sqrt(base) (measured as an angle)."""
+    d, base, p = 16, 10000.0, 5
+    x = np.zeros((1, 1, 1, d), np.float32)
+    x[..., 0] = 1.0
+    x[..., d // 4] = 1.0
+    y = oracle.rope(x, np.array([[p]], np.int32), base=base)[0, 0, 0]
+    ang0 = math.atan2(y[d // 2], y[0])
+    ang4 = math.atan2(y[d // 4 + d // 2], y[d // 4])
+    assert abs(math.remainder(ang0 - p, 2 * math.pi)) <= 1e-12
+    assert abs(ang4 - p / math.sqrt(base)) <= 1e-12
+
+
+def test_softcap_array_matches_scalar_routine():
+    x = np.array([-1e4, -75.0, -30.0, -1.5, 0.0, 1e-6, 2.0, 29.0, 300.0], np.float32)
+    got = oracle.softcap_array(x, 30.0)
+    for xi, gi in zip(x, got):
+        assert gi == oracle.softcap(float(xi), 30.0)
+    assert np.all(np.abs(got) < 30.0 + 1e-12)
