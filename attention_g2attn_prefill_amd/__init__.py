@@ -1,4 +1,5 @@
-"""Gemma 2 attention layer for MI355X (gfx950): prefill, decode and paged decode.
+"""Gemma 2 attention layer for MI355X (gfx950): prefill, decode and paged decode,
+plus the steps on either side of it (rotary embedding, final-logit soft-cap).
 
 The compute path is the C-ABI library libg2attn.so (hand-written HIP kernels);
 this package is a thin ctypes binding over it plus a seeded input generator
@@ -7,7 +8,7 @@ if the library has not been built: there is no CPU fallback.
 """
 _BINDING_NAMES = (
     "prefill", "prefill_lse", "decode", "decode_workspace_bytes", "check_args", "status_string",
-    "decode_paged", "decode_paged_workspace_bytes", "check_paged_args",
+    "decode_paged", "decode_paged_workspace_bytes", "check_paged_args", "rope_", "softcap_",
     "library_path", "G2attnError", "lib",
 )
 

@@ -41,6 +41,10 @@ lib.g2attn_decode_paged_workspace_bytes.argtypes = [_I] * 5
 lib.g2attn_decode_paged_workspace_bytes.restype = ctypes.c_size_t
 lib.g2attn_check_paged_args.argtypes = [_I] * 10
 lib.g2attn_check_paged_args.restype = _I
+lib.g2attn_rope.argtypes = [_vp, _vp, _I, _I, _I, _I, _F, _I, _vp]
+lib.g2attn_rope.restype = _I
+lib.g2attn_softcap.argtypes = [_vp, ctypes.c_size_t, _F, _I, _vp]
+lib.g2attn_softcap.restype = _I
 lib.g2attn_check_args.argtypes = [_I] * 10
 lib.g2attn_check_args.restype = _I
 lib.g2attn_status_string.argtypes = [_I]
@@ -221,3 +225,30 @@ def decode_paged(q, k_pool, v_pool, block_table, kv_lens, *, query_scale, softca
     if st != 0:
         raise G2attnError(st, "g2attn_decode_paged")
     return out
+
+
+def rope_(x, positions, *, base=10000.0, stream=None):
+    """Rotary embedding of x (B, T, NH, d) in place at positions int32 (B, T)
+    on the GPU; pair i is (x[..., i], x[..., i + d/2]) turned by
+    pos * base**(-2i/d).  Returns x."""
+    B, T, NH, d = x.shape
+    if x.dtype not in _DTYPES:
+        raise TypeError("x must be bfloat16 or float32")
+    if positions.dtype != torch.int32 or tuple(positions.shape) != (B, T):
+        raise TypeError("positions must be int32 of shape (B, T)")
+    st = lib.g2attn_rope(_dev(x, "x"), _dev(positions, "positions"), B, T, NH, d, float(base),
+                         _DTYPES[x.dtype], _stream_handle(stream))
+    if st != 0:
+        raise G2attnError(st, "g2attn_rope")
+    return x
+
+
+def softcap_(x, cap=30.0, stream=None):
+    """Final-logit soft-cap in place: x = cap * tanh(x / cap).  Returns x."""
+    if x.dtype not in _DTYPES:
+        raise TypeError("x must be bfloat16 or float32")
+    st = lib.g2attn_softcap(_dev(x, "x"), x.numel(), float(cap), _DTYPES[x.dtype],
+                            _stream_handle(stream))
+    if st != 0:
+        raise G2attnError(st, "g2attn_softcap")
+    return x

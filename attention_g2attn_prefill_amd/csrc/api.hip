@@ -158,4 +158,24 @@ int g2attn_decode_paged(const void* q, const void* k_pool, const void* v_pool, v
   return e == hipSuccess ? G2_OK : G2_ERR_LAUNCH;
 }
 
+int g2attn_rope(void* x, const int32_t* positions, int B, int T, int NH, int d, float base,
+                int dtype, hipStream_t stream) {
+  if (B <= 0 || T <= 0 || NH <= 0) return G2_ERR_ARG;
+  if (!(base > 1.0f) || __builtin_isinf(base)) return G2_ERR_ARG;
+  if (dtype != G2_BF16 && dtype != G2_F32) return G2_ERR_ARG;
+  if (d != 64 && d != 128 && d != 256) return G2_ERR_UNSUPPORTED;
+  if (!x || !positions) return G2_ERR_ARG;
+  if (!aligned16(x) || (reinterpret_cast<uintptr_t>(positions) & 3u) != 0) return G2_ERR_ALIGN;
+  g2::RopeLaunch L{x, positions, B, T, NH, d, base, dtype};
+  return g2::launch_rope(L, stream) == hipSuccess ? G2_OK : G2_ERR_LAUNCH;
+}
+
+int g2attn_softcap(void* x, size_t n, float cap, int dtype, hipStream_t stream) {
+  if (dtype != G2_BF16 && dtype != G2_F32) return G2_ERR_ARG;
+  if (n == 0 || !(cap > 0.0f) || __builtin_isinf(cap)) return G2_OK;  // nothing to do
+  if (!x) return G2_ERR_ARG;
+  if (!aligned16(x)) return G2_ERR_ALIGN;
+  return g2::launch_softcap(x, n, cap, dtype, stream) == hipSuccess ? G2_OK : G2_ERR_LAUNCH;
+}
+
 }  // extern "C"

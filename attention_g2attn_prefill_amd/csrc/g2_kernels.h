@@ -54,6 +54,16 @@ inline int decode_call_splits(const DecodeLaunch& L) {
   return (int)((seen + kDecodeChunk - 1) / kDecodeChunk);
 }
 
+struct RopeLaunch {
+  void* x;                  // (B, T, NH, d), rotated in place
+  const int32_t* positions;  // (B, T)
+  int B, T, NH, d;
+  float base;
+  int dtype;
+};
+
+hipError_t launch_rope(const RopeLaunch& L, hipStream_t stream);
+hipError_t launch_softcap(void* x, size_t n, float cap, int dtype, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillLaunch& L, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillLaunch& L, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& L, int dtype, hipStream_t stream);

@@ -8,7 +8,10 @@ One step = the whole hot path on seeded synthetic inputs shaped like Gemma 2 9B:
   and a local 4096-slot ring; then the same decode against a paged cache
   (16-token blocks at seeded random pool positions, one block table per
   sequence); and a chunked prefill: the last 2048 queries of the 9B batch
-  against its whole 8192-token cache (local and global).
+  against its whole 8192-token cache (local and global).  The steps on either
+  side of the attention call are timed after the steps, on their own: the
+  rotary embedding of the 9B prefill's Q and K, and the final-logit soft-cap
+  (30) over the prefill batch's vocabulary logits (2*8192 x 256000, bf16).
 
 Reported (one JSON line):
   value    prefill effective TFLOP/s = algorithmic FLOPs of the pair / prefill
@@ -106,6 +109,43 @@ def copy_gbs(dev, mib=1024, reps=5):
     secs = e0.elapsed_time(e1) * 1e-3 / reps
     del src, dst
     return 2.0 * n / secs / 1e9
+
+
+def time_adjacent(g2, qd, kd, dev, stream, reps=10, vocab=256000):
+    """HBM rate of the rotary embedding (Q and K in place) and of the final
+    soft-cap (logits in place): bytes read + written / kernel time."""
+    import torch
+    B, T = qd.shape[0], qd.shape[1]
+    pos = torch.arange(T, dtype=torch.int32, device=dev).repeat(B, 1).contiguous()
+    q2, k2 = qd.clone(), kd.clone()
+    logits = torch.randn((B * T, vocab), dtype=torch.bfloat16, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    g2.rope_(q2, pos, stream=stream)
+    g2.rope_(k2, pos, stream=stream)
+    g2.softcap_(logits, 30.0, stream=stream)
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(reps):
+        g2.rope_(q2, pos, stream=stream)
+        g2.rope_(k2, pos, stream=stream)
+    ev[1].record(stream)
+    for _ in range(reps):
+        g2.softcap_(logits, 30.0, stream=stream)
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    t_rope = ev[0].elapsed_time(ev[1]) * 1e-3 / reps
+    t_cap = ev[1].elapsed_time(ev[2]) * 1e-3 / reps
+    rope_bytes = 2.0 * (q2.numel() + k2.numel()) * q2.element_size()
+    cap_bytes = 2.0 * logits.numel() * logits.element_size()
+    del q2, k2, logits
+    return {"rope": {"metric": "rotary embedding of Q and K, GB/s", "value": round(rope_bytes / t_rope / 1e9, 1),
+                     "frac_of_hbm_peak": round(rope_bytes / t_rope / 1e9 / PEAK_HBM_GBS, 4),
+                     "ms": round(t_rope * 1e3, 4), "bytes": rope_bytes},
+            "final_softcap": {"metric": "final-logit soft-cap, GB/s",
+                              "value": round(cap_bytes / t_cap / 1e9, 1),
+                              "frac_of_hbm_peak": round(cap_bytes / t_cap / 1e9 / PEAK_HBM_GBS, 4),
+                              "ms": round(t_cap * 1e3, 4), "bytes": cap_bytes,
+                              "shape": [int(B * T), vocab]}}
 
 
 def measured_traffic(src_hash, key="traffic_bytes_per_launch"):
@@ -316,6 +356,7 @@ def main():
     med = np.median(ms, axis=0)
     mn = ms.min(axis=0)
 
+    adjacent = time_adjacent(g2, qd, kd, dev, stream, reps=10)
     copy_rate = copy_gbs(dev)
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
@@ -404,6 +445,7 @@ def main():
         "cpu_baseline": cpu,
         "decode": decode,
         "decode_paged": decode_paged,
+        "adjacent": adjacent,
         "prefill_chunk": {"metric": "chunked prefill eff. TFLOP/s", "value": round(chunk_tflops, 2),
                           "unit": "TFLOP/s", "chunk": CT, "cache": S,
                           "frac_of_bf16_peak": round(chunk_tflops / PEAK_BF16_TFLOPS, 4),

@@ -167,6 +167,31 @@ int g2attn_check_paged_args(int B, int H, int KVH, int d, int block_size,
                             int is_local, int dtype);
 
 /*
+ * Rotary position embedding of Q or K, in place (wikillm model card, "Method"
+ * item 5: Gemma 2 keeps Gemma 1's rotary embeddings; the pages give no
+ * formula, so the pair layout and base are this library's reading).
+ *   x         : (B, T, NH, d) device tensor of dtype; NH is H for queries and
+ *               KVH for keys.  Pair i < d/2 of every head vector is
+ *               (x[i], x[i + d/2]), rotated by the angle pos * base^(-2i/d):
+ *               (a, b) -> (a cos - b sin, b cos + a sin).
+ *   positions : device int32 (B, T), the absolute position of each token
+ *               (for a chunk of T tokens ending a cache of S: t + S - T).
+ *   base      : > 1 (10000 for the rotary embeddings of the Gemma family).
+ *   d         : 64, 128 or 256 (G2_ERR_UNSUPPORTED otherwise).
+ * x must be 16-byte aligned, positions 4-byte aligned.
+ */
+int g2attn_rope(void* x, const int32_t* positions, int B, int T, int NH, int d,
+                float base, int dtype, hipStream_t stream);
+
+/*
+ * Final-logit soft-cap in place: x[i] = cap * tanh(x[i] / cap) for the n
+ * elements of x (Gemma 2 Guide, section 1, second formula: the vocabulary
+ * logits are capped at 30).  cap <= 0 or +inf leaves x unchanged; n = 0 is a
+ * no-op.  x must be 16-byte aligned.
+ */
+int g2attn_softcap(void* x, size_t n, float cap, int dtype, hipStream_t stream);
+
+/*
  * Host-only validation of the scalar arguments of either entry point
  * (decode = 1 for decode), returning the status the call would return for
  * non-null, aligned pointers.  Touches no GPU.

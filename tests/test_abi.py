@@ -24,7 +24,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("g2attn_prefill", "g2attn_prefill_lse", "g2attn_decode", "g2attn_decode_workspace_bytes",
               "g2attn_check_args", "g2attn_status_string", "g2attn_decode_paged",
-              "g2attn_decode_paged_workspace_bytes", "g2attn_check_paged_args"):
+              "g2attn_decode_paged_workspace_bytes", "g2attn_check_paged_args",
+              "g2attn_rope", "g2attn_softcap"):
         assert n in names
 
 
@@ -145,3 +146,20 @@ def test_paged_entry_point_rejects_before_launching():
     # a local layer needs only the splits of its window: 64 positions here
     small = g2.decode_paged_workspace_bytes(2, 4, 64, 1, 64)
     assert lib.g2attn_decode_paged(*args(nbytes=small - 1)) == WS
+
+
+def test_adjacent_steps_reject_before_launching():
+    lib = g2.lib
+    a = _fake(0x10000)
+    null = ctypes.c_void_p(0)
+    assert lib.g2attn_rope(a, a, 2, 3, 4, 96, 10000.0, 0, null) == UNSUP
+    assert lib.g2attn_rope(a, a, 2, 3, 4, 128, 1.0, 0, null) == ARG      # base must exceed 1
+    assert lib.g2attn_rope(a, a, 0, 3, 4, 128, 10000.0, 0, null) == ARG
+    assert lib.g2attn_rope(null, a, 2, 3, 4, 128, 10000.0, 0, null) == ARG
+    assert lib.g2attn_rope(_fake(0x10008), a, 2, 3, 4, 128, 10000.0, 0, null) == ALIGN
+    assert lib.g2attn_rope(a, _fake(0x10002), 2, 3, 4, 128, 10000.0, 0, null) == ALIGN
+    assert lib.g2attn_softcap(a, 10, 30.0, 5, null) == ARG
+    assert lib.g2attn_softcap(_fake(0x10004), 10, 30.0, 0, null) == ALIGN
+    # nothing to do: no pointer is looked at, nothing is launched
+    assert lib.g2attn_softcap(null, 0, 30.0, 0, null) == OK
+    assert lib.g2attn_softcap(null, 10, 0.0, 0, null) == OK
