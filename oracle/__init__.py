@@ -61,6 +61,9 @@ def _load():
     lib.g2o_rope.restype = _I
     lib.g2o_softcap_array.argtypes = [_f32p, _f64p, ctypes.c_int64, _D]
     lib.g2o_softcap_array.restype = None
+    lib.g2o_prefill_backward.argtypes = [_f32p, _f32p, _f32p, _f32p, _f64p, _f64p, _f64p, _I,
+                                         _I, _I, _I, _I, _I, _D, _D, _I, _I]
+    lib.g2o_prefill_backward.restype = _I
     lib.g2o_threads.argtypes = []
     lib.g2o_threads.restype = _I
     _lib = lib
@@ -282,3 +285,22 @@ def softcap_array(x, cap):
     out = np.empty(x.shape, np.float64)
     _load().g2o_softcap_array(_ptr(x, _f32p), _ptr(out, _f64p), x.size, float(cap))
     return out
+
+
+def prefill_backward(q, k, v, dout, *, query_scale, softcap, window, is_local):
+    """Gradients (dq, dk, dv) in float64 of the prefill for an upstream
+    gradient dout (B,T,H,d) of its output."""
+    q, k, v, g = _f32(q), _f32(k), _f32(v), _f32(dout)
+    B, T, S, H, KVH, d = _shape_prefill(q, k, v)
+    if g.shape != q.shape:
+        raise OracleError("dout must match q")
+    dq = np.empty(q.shape, np.float64)
+    dk = np.empty(k.shape, np.float64)
+    dv = np.empty(v.shape, np.float64)
+    st = _load().g2o_prefill_backward(_ptr(q, _f32p), _ptr(k, _f32p), _ptr(v, _f32p),
+                                      _ptr(g, _f32p), _ptr(dq, _f64p), _ptr(dk, _f64p),
+                                      _ptr(dv, _f64p), B, T, S, H, KVH, d, query_scale, softcap,
+                                      window, int(bool(is_local)))
+    if st != 0:
+        raise OracleError(f"oracle rejected arguments (status {st})")
+    return dq, dk, dv

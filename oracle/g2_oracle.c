@@ -395,6 +395,84 @@ int g2o_decode_paged(const float* q, const float* k_pool, const float* v_pool,
   return G2O_OK;
 }
 
+/* Backward pass of the prefill (Gemma 2 Guide, "Deep Dive" item 1: the cap's
+ * derivative is 1 - tanh^2(x / cap)).  With y_j = x_j / cap, s_j = cap tanh y_j
+ * and the softmax weights w_j of a row, for an upstream gradient dO of the
+ * output row:
+ *   dv_j += w_j dO,   D = <dO, out>,   ds_j = w_j (<dO, v_j> - D),
+ *   dx_j = ds_j (1 - tanh^2 y_j)   (dx_j = ds_j when the cap is disabled),
+ *   dq   = query_scale * sum_j dx_j k_j,   dk_j += query_scale * dx_j q.
+ * q, dout, dq: (B,T,H,d); k, v, dk, dv: (B,S,KVH,d).  dk and dv sum over the
+ * query heads of a group and over every row that sees the key.  The rows of one
+ * (batch, K/V head) group run in order, so every sum has a fixed order. */
+int g2o_prefill_backward(const float* q, const float* k, const float* v,
+                         const float* dout, double* dq, double* dk, double* dv,
+                         int B, int T, int S, int H, int KVH, int d,
+                         double query_scale, double softcap, int window,
+                         int is_local) {
+  if (!check_shapes(B, T, S, H, KVH, d, window, is_local)) return G2O_ERR_ARG;
+  const int G = H / KVH;
+  const int use_cap = (softcap > 0.0) && !isinf(softcap);
+  memset(dk, 0, sizeof(double) * (size_t)B * S * KVH * d);
+  memset(dv, 0, sizeof(double) * (size_t)B * S * KVH * d);
+#pragma omp parallel
+  {
+    const float** k_rows = (const float**)malloc(sizeof(float*) * (size_t)S);
+    const float** v_rows = (const float**)malloc(sizeof(float*) * (size_t)S);
+    unsigned char* allowed = (unsigned char*)malloc((size_t)S);
+    double* sc = (double*)malloc(sizeof(double) * (size_t)S);
+    double* w = (double*)malloc(sizeof(double) * (size_t)S);
+    double* o = (double*)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t bg = 0; bg < (int64_t)B * KVH; ++bg) {
+      const int b = (int)(bg / KVH), g = (int)(bg % KVH);
+      for (int hh = 0; hh < G; ++hh) {
+        const int h = g * G + hh;
+        for (int t = 0; t < T; ++t) {
+          prefill_row_setup(k, T, S, H, KVH, d, window, is_local, b, t, h, k_rows,
+                            allowed);
+          for (int64_t j = 0; j < S; ++j)
+            v_rows[j] = v + (((int64_t)b * S + j) * KVH + g) * d;
+          const int64_t r = ((int64_t)b * T + t) * H + h;
+          const float* qrow = q + r * d;
+          const float* gout = dout + r * d;
+          row_logits(qrow, k_rows, allowed, S, d, query_scale, softcap, sc);
+          row_softmax(sc, S, w);
+          row_output(v_rows, w, S, d, o);
+          double D = 0.0;
+          for (int e = 0; e < d; ++e) D += (double)gout[e] * o[e];
+          double* dqr = dq + r * d;
+          for (int e = 0; e < d; ++e) dqr[e] = 0.0;
+          for (int64_t j = 0; j < S; ++j) {
+            if (w[j] == 0.0) continue;
+            const float* vr = v_rows[j];
+            const float* kr = k_rows[j];
+            double dw = 0.0;
+            for (int e = 0; e < d; ++e) dw += (double)gout[e] * (double)vr[e];
+            const double ds = w[j] * (dw - D);
+            const double th = use_cap ? sc[j] / softcap : 0.0;
+            const double dx = use_cap ? ds * (1.0 - th * th) : ds;
+            double* dkr = dk + (((int64_t)b * S + j) * KVH + g) * d;
+            double* dvr = dv + (((int64_t)b * S + j) * KVH + g) * d;
+            for (int e = 0; e < d; ++e) {
+              dqr[e] += query_scale * dx * (double)kr[e];
+              dkr[e] += query_scale * dx * (double)qrow[e];
+              dvr[e] += w[j] * (double)gout[e];
+            }
+          }
+        }
+      }
+    }
+    free(k_rows);
+    free(v_rows);
+    free(allowed);
+    free(sc);
+    free(w);
+    free(o);
+  }
+  return G2O_OK;
+}
+
 /* Rotary position embedding (wikillm model card, "Method" item 5: rotary
  * embeddings carried over from Gemma 1; the pages give no formula).  Reading:
  * the rotary embedding of Su et al. with pair i of a head vector formed by

@@ -642,3 +642,77 @@ def test_softcap_array_matches_scalar_routine():
     for xi, gi in zip(x, got):
         assert gi == oracle.softcap(float(xi), 30.0)
     assert np.all(np.abs(got) < 30.0 + 1e-12)
+
+
+# ---- backward pass (Guide "Deep Dive" item 1: d/dx cap*tanh(x/cap) = 1 - tanh^2)
+
+def _grid_case(seed, B, T, S, H, KVH, d, span=3.0):
+    """Inputs on a 2^-6 grid inside [-span, span], so x +- 2^-12 is exact in float32."""
+    rng = np.random.default_rng(seed)
+    f = lambda shape: (np.round(rng.uniform(-span, span, size=shape) * 64) / 64).astype(np.float32)
+    return f((B, T, H, d)), f((B, S, KVH, d)), f((B, S, KVH, d)), f((B, T, H, d))
+
+
+@pytest.mark.parametrize("is_local,window,cap", [(False, 4096, 5.0), (True, 3, 5.0),
+                                                  (True, 4, 0.0), (False, 1, 2.0)])
+def test_backward_matches_central_differences(is_local, window, cap):
+    """Every gradient entry of L = sum(out * R) against central differences of
+    the (pinned) forward oracle, step 2^-12."""
+    B, T, S, H, KVH, d = 1, 6, 7, 4, 2, 4
+    q, k, v, R = _grid_case(281, B, T, S, H, KVH, d)
+    kw = dict(query_scale=0.5, softcap=cap, window=window, is_local=is_local)
+    dq, dk, dv = oracle.prefill_backward(q, k, v, R, **kw)
+    h = 2.0 ** -12
+    R64 = R.astype(np.float64)
+
+    def loss(qq, kk, vv):
+        return float(np.sum(oracle.prefill(qq, kk, vv, **kw) * R64))
+
+    for name, arr, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in np.ndindex(arr.shape):
+            plus, minus = arr.copy(), arr.copy()
+            plus[idx] += np.float32(h)
+            minus[idx] -= np.float32(h)
+            args = {"q": (q, k, v), "k": (q, k, v), "v": (q, k, v)}[name]
+            ap = [plus if a is arr else a for a in args]
+            am = [minus if a is arr else a for a in args]
+            fd = (loss(*ap) - loss(*am)) / (2 * h)
+            assert abs(fd - grad[idx]) <= 1e-6 * (1.0 + abs(fd)), (name, idx, fd, grad[idx])
+
+
+@pytest.mark.parametrize("T,S", [(9, 9), (5, 11)])
+@pytest.mark.parametrize("is_local,window", [(False, 1), (True, 3)])
+def test_backward_cap_off_matches_library_autograd(T, S, is_local, window):
+    """With the cap disabled the gradients are those of plain attention: torch
+    autograd through scaled_dot_product_attention in float64, K/V repeated per
+    query head (their gradients summed back over the group)."""
+    B, H, KVH, d = 2, 4, 2, 8
+    q, k, v = rand((B, T, H, d), 291, mul=2.0), rand((B, S, KVH, d), 292), rand((B, S, KVH, d), 293)
+    R = rand((B, T, H, d), 294)
+    dq, dk, dv = oracle.prefill_backward(q, k, v, R, query_scale=0.4, softcap=0.0, window=window,
+                                         is_local=is_local)
+    G = H // KVH
+    qt = torch.tensor(q.astype(np.float64), requires_grad=True)
+    kt = torch.tensor(k.astype(np.float64), requires_grad=True)
+    vt = torch.tensor(v.astype(np.float64), requires_grad=True)
+    mask = torch.from_numpy(page_mask(T, S, window, is_local))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt.permute(0, 2, 1, 3), kt.permute(0, 2, 1, 3).repeat_interleave(G, dim=1),
+        vt.permute(0, 2, 1, 3).repeat_interleave(G, dim=1), attn_mask=mask, scale=0.4)
+    (o.permute(0, 2, 1, 3) * torch.from_numpy(R.astype(np.float64))).sum().backward()
+    assert np.max(np.abs(dq - qt.grad.numpy())) <= 1e-12
+    assert np.max(np.abs(dk - kt.grad.numpy())) <= 1e-12
+    assert np.max(np.abs(dv - vt.grad.numpy())) <= 1e-12
+
+
+def test_backward_window_one_closed_form():
+    """A row that sees only itself has weight 1: dv of a key is the sum of its
+    group's upstream gradients at that position, and dq = dk = 0."""
+    B, T, H, KVH, d = 1, 6, 4, 2, 8
+    q, k, v = rand((B, T, H, d), 301, mul=3.0), rand((B, T, KVH, d), 302), rand((B, T, KVH, d), 303)
+    R = rand((B, T, H, d), 304)
+    dq, dk, dv = oracle.prefill_backward(q, k, v, R, query_scale=0.5, softcap=50.0, window=1,
+                                         is_local=True)
+    assert np.max(np.abs(dq)) <= 1e-15 and np.max(np.abs(dk)) <= 1e-15
+    want = R.astype(np.float64).reshape(B, T, KVH, H // KVH, d).sum(axis=3)
+    assert np.max(np.abs(dv - want)) <= 1e-14
