@@ -7,7 +7,7 @@ this package is a thin ctypes binding over it plus a seeded input generator
 if the library has not been built: there is no CPU fallback.
 """
 _BINDING_NAMES = (
-    "prefill", "prefill_lse", "decode", "decode_workspace_bytes", "check_args", "status_string",
+    "prefill", "prefill_lse", "prefill_backward", "decode", "decode_workspace_bytes", "check_args", "status_string",
     "decode_paged", "decode_paged_workspace_bytes", "check_paged_args", "rope_", "softcap_",
     "library_path", "G2attnError", "lib",
 )

@@ -41,6 +41,11 @@ lib.g2attn_decode_paged_workspace_bytes.argtypes = [_I] * 5
 lib.g2attn_decode_paged_workspace_bytes.restype = ctypes.c_size_t
 lib.g2attn_check_paged_args.argtypes = [_I] * 10
 lib.g2attn_check_paged_args.restype = _I
+lib.g2attn_prefill_backward.argtypes = [_vp] * 9 + [_I] * 6 + [_F, _F, _I, _I, _I, _vp,
+                                                                ctypes.c_size_t, _vp]
+lib.g2attn_prefill_backward.restype = _I
+lib.g2attn_prefill_backward_workspace_bytes.argtypes = [_I, _I, _I]
+lib.g2attn_prefill_backward_workspace_bytes.restype = ctypes.c_size_t
 lib.g2attn_rope.argtypes = [_vp, _vp, _I, _I, _I, _I, _F, _I, _vp]
 lib.g2attn_rope.restype = _I
 lib.g2attn_softcap.argtypes = [_vp, ctypes.c_size_t, _F, _I, _vp]
@@ -252,3 +257,36 @@ def softcap_(x, cap=30.0, stream=None):
     if st != 0:
         raise G2attnError(st, "g2attn_softcap")
     return x
+
+
+def prefill_backward(q, k, v, out, dout, lse, *, query_scale, softcap=50.0, window=4096,
+                     is_local, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of the prefill for an upstream gradient dout of
+    its output; out and lse come from prefill_lse() with the same arguments.
+    bfloat16 only."""
+    B, T, H, d = q.shape
+    Bk, S, KVH, dk_ = k.shape
+    if (Bk, dk_) != (B, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch between q and k/v")
+    for t, name in ((out, "out"), (dout, "dout")):
+        if tuple(t.shape) != tuple(q.shape) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q")
+    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("the backward pass takes bfloat16 tensors")
+    if tuple(lse.shape) != (B, H, T) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 of shape (B, H, T)")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = int(lib.g2attn_prefill_backward_workspace_bytes(B, T, H))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = lib.g2attn_prefill_backward(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(dout, "dout"),
+        _dev(lse, "lse"), _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"), B, T, S, H, KVH, d,
+        float(query_scale), float(softcap), int(window), int(bool(is_local)), G2_BF16,
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream_handle(stream))
+    if st != 0:
+        raise G2attnError(st, "g2attn_prefill_backward")
+    return dq, dk, dv

@@ -178,4 +178,29 @@ int g2attn_softcap(void* x, size_t n, float cap, int dtype, hipStream_t stream) 
   return g2::launch_softcap(x, n, cap, dtype, stream) == hipSuccess ? G2_OK : G2_ERR_LAUNCH;
 }
 
+size_t g2attn_prefill_backward_workspace_bytes(int B, int T, int H) {
+  if (B <= 0 || T <= 0 || H <= 0) return 0;
+  return (size_t)B * H * T * sizeof(float);
+}
+
+int g2attn_prefill_backward(const void* q, const void* k, const void* v, const void* out,
+                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                            int B, int T, int S, int H, int KVH, int d, float query_scale,
+                            float softcap, int window, int is_local, int dtype, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  int st = check_scalars(B, T, S, H, KVH, d, window, is_local, dtype, 0);
+  if (st != G2_OK) return st;
+  if (dtype != G2_BF16) return G2_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv) return G2_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return G2_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return G2_ERR_ALIGN;
+  if (!workspace || workspace_bytes < (size_t)B * H * T * sizeof(float)) return G2_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0) return G2_ERR_ALIGN;
+  g2::BackwardLaunch L{q, k, v, out, dout, lse, dq, dk, dv, B, T, S, H, KVH, d,
+                       query_scale, softcap, window, is_local, workspace};
+  return g2::launch_prefill_backward(L, stream) == hipSuccess ? G2_OK : G2_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -1,0 +1,571 @@
+// Backward pass of the prefill, bf16 storage, fp32 accumulation, on gfx950
+// MFMA (v_mfma_f32_16x16x32_bf16).
+//
+// What it differentiates (Gemma 2 Guide, "Deep Dive" item 1, the cap's
+// derivative 1 - tanh^2(x/cap); wikillm model card "Method" for the layer):
+// for a row with capped logits s_j = cap tanh(x_j / cap), x_j = qs <q, k_j>,
+// weights w_j = exp(s_j - lse) and upstream gradient dO,
+//   dv_j += w_j dO,  D = <dO, out>,  ds_j = w_j (<dO, v_j> - D),
+//   dx_j = ds_j (1 - tanh^2),  dq = qs sum_j dx_j k_j,  dk_j += qs dx_j q.
+// lse is the forward's log-sum-exp (g2attn_prefill_lse), so nothing of the
+// forward is stored but the output and lse.
+//
+// Three kernels:
+//  * prep: D per row (B, H, T) into the workspace;
+//  * dK/dV, key-stationary: a workgroup owns 64 keys of one K/V head (16 per
+//    wave).  Each wave keeps its keys' K and V fragments and its dK^T, dV^T
+//    accumulators in registers and streams 32-row tiles of Q and dO (both
+//    heads of the GQA pair) through double-buffered LDS.  Per tile:
+//    S = Q K^T and dP = dO V^T with the tile as A operand (ds_read_b128) and
+//    the stationary fragments as B; each lane then holds one key column and
+//    eight query rows, so P and dS are formed in registers and feed
+//    dV^T += dO^T P and dK^T += Q^T dS with the tile's transpose (the LDS
+//    transpose read) as A operand;
+//  * dQ, query-stationary: a workgroup owns 32 positions of both heads (16 rows
+//    per wave) and streams 32-key tiles of K and V, like the forward:
+//    S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T.
+// Every tile uses one 16-byte-chunk swizzle, byte (c/4)*R*64 + r*64 +
+// 16*((c%4) ^ ((r/4)%4)) for chunk c of row r of an R-row tile: the row reads
+// are conflict-free; the transpose reads of the same tile share banks in part.
+#include "g2_device.h"
+#include "g2_kernels.h"
+
+namespace g2 {
+
+typedef short s16x4_b __attribute__((ext_vector_type(4)));
+typedef short s16x8_b __attribute__((ext_vector_type(8)));
+#define G2B_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define G2B_LDS_S16X4(p) ((__attribute__((address_space(3))) s16x4_b*)(p))
+
+struct BwdArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const bf16* out;
+  const bf16* dout;
+  const float* lse;  // (B, H, T), natural log
+  float* dsum;       // (B, H, T): D = <dO, out>, written by the prep kernel
+  bf16* dq;
+  bf16* dk;
+  bf16* dv;
+  int B, T, S, H, KVH;
+  CapConsts cap;
+  float query_scale;
+  int window, is_local;
+};
+
+__device__ __forceinline__ int swz_rows(int r) { return (r >> 2) & 3; }
+
+// Transpose-read lane offset inside an R-row tile for column block parity
+// `par`: lane reads row 4*lq + l16/4 at dims 16*db + 4*(l16%4).
+__device__ __forceinline__ int tr_lane_off(int l16, int lq, int par) {
+  return (4 * lq + (l16 >> 2)) * 64 + 16 * (((2 * par) + ((l16 & 3) >> 1)) ^ lq) + 8 * (l16 & 1);
+}
+
+// A-operand fragment of rows (tile rows 32*ks + 4*lq + j and + 16) x dims
+// 16*db + l16, through two transpose reads.
+template <int R>
+__device__ __forceinline__ bf16x8 read_tr(const char* tile, int db, int ks, const int (&tr)[2]) {
+  const char* p = tile + (db >> 1) * (R * 64) + (32 * ks) * 64 + tr[db & 1];
+  const s16x4_b a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G2B_LDS_S16X4(p));
+  const s16x4_b b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G2B_LDS_S16X4(p + 16 * 64));
+  const s16x8_b v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Gradient of the capped logit with respect to the raw score <q, k>, times
+// the softmax term: dS * (1 - tanh^2) * qs, from the capped logit s2 in log2
+// units (tanh = s2 / (cap log2 e)).
+template <int CAP>
+__device__ __forceinline__ float cap_grad(float ds, float s2, float inv_cout, float qs) {
+  if constexpr (CAP == kCapNone) {
+    return ds * qs;
+  } else {
+    const float t = s2 * inv_cout;
+    return ds * ((1.0f - t) * (1.0f + t)) * qs;
+  }
+}
+
+template <int CAP>
+__device__ __forceinline__ float capped(float x, float k_in, float c_out) {
+  if constexpr (CAP == kCapFast) return capped_log2_fast(x, k_in, c_out);
+  else if constexpr (CAP == kCapAccurate) return capped_log2_accurate(x, k_in, c_out);
+  else return x * k_in;
+}
+
+// ---------------------------------------------------------------- prep
+// D[b, h, t] = <dO[b, t, h, :], out[b, t, h, :]>; a group of D/8 lanes per row.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  constexpr int LPR = D / 8;
+  const long row = ((long)blockIdx.x * 256 + threadIdx.x) / LPR;  // (b, t, h) flat
+  const int sub = threadIdx.x % LPR;
+  const long rows = (long)a.B * a.T * a.H;
+  const bool live = row < rows;
+  float s = 0.f;
+  if (live) {
+    const u32x4 go = *reinterpret_cast<const u32x4*>(a.dout + row * D + sub * 8);
+    const u32x4 oo = *reinterpret_cast<const u32x4*>(a.out + row * D + sub * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s = __builtin_fmaf(bf16_lo_to_f32(go[e]), bf16_lo_to_f32(oo[e]), s);
+      s = __builtin_fmaf(bf16_hi_to_f32(go[e]), bf16_hi_to_f32(oo[e]), s);
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) s += shfl_xor(s, m);
+  if (live && sub == 0) {
+    const int h = (int)(row % a.H);
+    const int t = (int)((row / a.H) % a.T);
+    const int b = (int)(row / ((long)a.H * a.T));
+    a.dsum[((size_t)b * a.H + h) * a.T + t] = s;
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+template <int D, int G, int CAP>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int QT = 32;               // query rows per tile
+  constexpr int KB = 64;               // keys per workgroup
+  constexpr int KK = D / 32;           // k-steps over d
+  constexpr int DB = D / 16;           // 16-row blocks of dK^T, dV^T
+  constexpr int TILE = QT * D * 2;     // bytes of a Q or dO tile
+  constexpr int CPW = TILE / 1024 / 4; // wave-wide 1 KiB copies per wave and tile
+  constexpr int RG = QT / 16;          // 16-row groups per tile
+  static_assert(CPW >= 1, "tile copies split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) char lds[2][2][TILE];  // [stage][Q | dO]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15;
+  const int lq = lane >> 4;
+  const int T = a.T, S = a.S, H = a.H, KVH = a.KVH;
+  const int nbg = a.B * KVH;
+  const int kb_i = blockIdx.x / nbg;  // key block: the first ones are seen by the most rows
+  const int bg = blockIdx.x % nbg;
+  const int b = bg / KVH, g = bg % KVH;
+  const int j0 = kb_i * KB;
+  const int jw = j0 + 16 * wave;      // this wave's first key
+  const int off = S - T;
+  const int win = a.window;
+
+  // stationary B operands: key jw + l16, dims 32*kk + 8*lq .. +7
+  const size_t kv_row = (size_t)KVH * D;
+  bf16x8 kfr[KK], vfr[KK];
+  {
+    const int j = jw + l16;
+    const bf16* kr = a.k + ((size_t)b * S * KVH + g) * D + (size_t)(j < S ? j : 0) * kv_row + lq * 8;
+    const bf16* vr = a.v + ((size_t)b * S * KVH + g) * D + (size_t)(j < S ? j : 0) * kv_row + lq * 8;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 wk = {0u, 0u, 0u, 0u}, wv = {0u, 0u, 0u, 0u};
+      if (j < S) {
+        wk = *reinterpret_cast<const u32x4*>(kr + kk * 32);
+        wv = *reinterpret_cast<const u32x4*>(vr + kk * 32);
+      }
+      kfr[kk] = __builtin_bit_cast(bf16x8, wk);
+      vfr[kk] = __builtin_bit_cast(bf16x8, wv);
+    }
+  }
+  f32x4 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dk[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // query rows that see any of the workgroup's keys: p >= j0 and, on a local
+  // layer, p <= j0 + KB - 1 + win - 1
+  const int t_lo = (max(0, j0 - off) / QT) * QT;
+  const int t_hi = a.is_local ? min(T - 1, j0 + KB - 1 + win - 1 - off) : T - 1;
+  const int n_pos = (t_hi - t_lo) / QT + 1;  // tiles per head
+  const int n_tiles = G * n_pos;
+
+  // tile copies (rows t of head h; lanes past T copy nothing)
+  const unsigned q_row_bytes = (unsigned)H * D * 2u;
+  const unsigned dma_rl = lane >> 2;
+  const unsigned dma_lane = dma_rl * q_row_bytes + (((lane & 3) ^ swz_rows(dma_rl)) * 16u);
+  auto issue = [&](char (*__restrict__ dst)[TILE], int i) __attribute__((always_inline)) {
+    const int hh = i / n_pos;
+    const int t0 = t_lo + (i % n_pos) * QT;
+    const int h = g * G + hh;
+    const char* qb = reinterpret_cast<const char*>(a.q + ((size_t)b * T * H + h) * D);
+    const char* ob = reinterpret_cast<const char*>(a.dout + ((size_t)b * T * H + h) * D);
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int n = wave + c * 4;
+      const int cg = n / RG, r0 = 16 * (n % RG);
+      const size_t uni = (size_t)(t0 + r0) * q_row_bytes + 64u * cg;
+      const char* rq = qb + uni;
+      const char* ro = ob + uni;
+      unsigned lo = dma_lane;
+      asm volatile("" : "+s"(rq));
+      asm volatile("" : "+s"(ro));
+      asm volatile("" : "+v"(lo));
+      if (t0 + r0 + (int)dma_rl < T) {
+        __builtin_amdgcn_global_load_lds(rq + lo, G2B_LDS(&dst[0][n * 1024]), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(ro + lo, G2B_LDS(&dst[1][n * 1024]), 16, 0, 0);
+      }
+    }
+  };
+
+  const int k_lane = l16 * 64 + ((lq ^ swz_rows(l16)) << 4);
+  const int tr[2] = {tr_lane_off(l16, lq, 0), tr_lane_off(l16, lq, 1)};
+  const float k_in = a.cap.k_in, c_out = a.cap.c_out;
+  const float inv_cout = c_out > 0.f ? 1.0f / c_out : 0.f;
+  const float qs = a.query_scale;
+  constexpr float kLog2eF = 1.4426950408889634f;
+
+  auto compute = [&](const char (*__restrict__ buf)[TILE], int i) __attribute__((always_inline)) {
+    const int hh = i / n_pos;
+    const int t0 = t_lo + (i % n_pos) * QT;
+    const int h = g * G + hh;
+    const int p0 = t0 + off;
+    const int p_last = min(t0 + QT - 1, T - 1) + off;
+    if (jw > p_last || jw >= S) return;
+    if (a.is_local && jw + 15 <= p0 - win) return;
+    const bool need_mask = (jw + 15 > p0) || (t0 + QT > T) || (jw + 16 > S) ||
+                           (a.is_local && jw <= p_last - win);
+    const char* qt = buf[0];
+    const char* ot = buf[1];
+    // S = Q K^T and dP = dO V^T: rows = queries (A from the tile), cols = keys
+    f32x4 sc[2], dp[2];
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qt + kk * (QT * 64) + qb * 1024 + k_lane);
+        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(ot + kk * (QT * 64) + qb * 1024 + k_lane);
+        sc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kfr[kk], kk == 0 ? zero4 : sc[qb], 0, 0, 0);
+        dp[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, vfr[kk], kk == 0 ? zero4 : dp[qb], 0, 0, 0);
+      }
+    }
+    // P and dS for this lane's key column and its 8 query rows
+    const float* lse_row = a.lse + ((size_t)b * H + h) * T;
+    const float* d_row = a.dsum + ((size_t)b * H + h) * T;
+    const int j = jw + l16;
+    float pv[2][4], dsv[2][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = t0 + 16 * qb + 4 * lq + e;
+        const int tc = t < T ? t : T - 1;
+        const float l2 = lse_row[tc] * kLog2eF;
+        const float dd = d_row[tc];
+        const float s2 = capped<CAP>(sc[qb][e], k_in, c_out);
+        float p = exp2_fast(s2 - l2);
+        float ds = cap_grad<CAP>(p * (dp[qb][e] - dd), s2, inv_cout, qs);
+        if (need_mask) {
+          const int p_ = t + off;
+          const bool vis = (t < T) & (j < S) & (j <= p_) & ((j > p_ - win) | !a.is_local);
+          p = vis ? p : 0.f;
+          ds = vis ? ds : 0.f;
+        }
+        pv[qb][e] = p;
+        dsv[qb][e] = ds;
+      }
+    }
+    u32x4 wp, wd;
+    wp[0] = pack_bf16x2(pv[0][0], pv[0][1]);
+    wp[1] = pack_bf16x2(pv[0][2], pv[0][3]);
+    wp[2] = pack_bf16x2(pv[1][0], pv[1][1]);
+    wp[3] = pack_bf16x2(pv[1][2], pv[1][3]);
+    wd[0] = pack_bf16x2(dsv[0][0], dsv[0][1]);
+    wd[1] = pack_bf16x2(dsv[0][2], dsv[0][3]);
+    wd[2] = pack_bf16x2(dsv[1][0], dsv[1][1]);
+    wd[3] = pack_bf16x2(dsv[1][2], dsv[1][3]);
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, wp);
+    const bf16x8 sb = __builtin_bit_cast(bf16x8, wd);
+    // dV^T += dO^T P, dK^T += Q^T dS (k = the tile's 32 query rows)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 oT = read_tr<QT>(ot, db, 0, tr);
+      const bf16x8 qT = read_tr<QT>(qt, db, 0, tr);
+      dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oT, pb, dv[db], 0, 0, 0);
+      dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qT, sb, dk[db], 0, 0, 0);
+    }
+  };
+
+  {
+    u32x4* z = reinterpret_cast<u32x4*>(&lds[0][0][0]);
+    for (int i = tid; i < (int)(sizeof(lds) / 16); i += 256) z[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  auto step = [&](const char (*__restrict__ cur)[TILE], char (*__restrict__ nxt)[TILE], int i) __attribute__((always_inline)) {
+    if (i + 1 < n_tiles) issue(nxt, i + 1);
+    compute(cur, i);
+  };
+  issue(lds[0], 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int i = 0; i < n_tiles; i += 2) {
+    step(lds[0], lds[1], i);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (i + 1 < n_tiles) {
+      step(lds[1], lds[0], i + 1);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  }
+
+  // dK, dV rows: key jw + l16, dims 16*db + 4*lq .. +3
+  const int j = jw + l16;
+  if (j < S) {
+    bf16* kr = a.dk + (((size_t)b * S + j) * KVH + g) * D + 4 * lq;
+    bf16* vr = a.dv + (((size_t)b * S + j) * KVH + g) * D + 4 * lq;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      u32x2 wk, wv;
+      wk[0] = pack_bf16x2(dk[db][0], dk[db][1]);
+      wk[1] = pack_bf16x2(dk[db][2], dk[db][3]);
+      wv[0] = pack_bf16x2(dv[db][0], dv[db][1]);
+      wv[1] = pack_bf16x2(dv[db][2], dv[db][3]);
+      *reinterpret_cast<u32x2*>(kr + db * 16) = wk;
+      *reinterpret_cast<u32x2*>(vr + db * 16) = wv;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+template <int D, int G, int CAP>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int BN = 32;               // keys per tile
+  constexpr int KK = D / 32;
+  constexpr int DB = D / 16;
+  constexpr int TILE = BN * D * 2;
+  constexpr int CPW = TILE / 1024 / 4;
+  constexpr int RG = BN / 16;
+  constexpr int WPH = 4 / G;           // waves per query head
+  constexpr int BMP = 16 * WPH;        // positions per workgroup
+  static_assert(CPW >= 1, "tile copies split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) char lds[2][2][TILE];  // [stage][K | V]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15;
+  const int lq = lane >> 4;
+  const int T = a.T, S = a.S, H = a.H, KVH = a.KVH;
+  const int nbg = a.B * KVH;
+  const int n_mb = (T + BMP - 1) / BMP;
+  const int mb = n_mb - 1 - (int)(blockIdx.x / nbg);  // heaviest first
+  const int bg = blockIdx.x % nbg;
+  const int b = bg / KVH, g = bg % KVH;
+  const int h = g * G + wave / WPH;
+  const int t0 = mb * BMP + (wave % WPH) * 16;  // this wave's first row
+  const int off = S - T;
+  const int win = a.window;
+
+  // stationary B operands: Q^T and dO^T of query t0 + l16, dims 32*kk + 8*lq
+  const int tq = t0 + l16;
+  bf16x8 qf[KK], of[KK];
+  {
+    const size_t r = ((size_t)b * T + (tq < T ? tq : 0)) * H + h;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 wq = {0u, 0u, 0u, 0u}, wo = {0u, 0u, 0u, 0u};
+      if (tq < T) {
+        wq = *reinterpret_cast<const u32x4*>(a.q + r * D + kk * 32 + lq * 8);
+        wo = *reinterpret_cast<const u32x4*>(a.dout + r * D + kk * 32 + lq * 8);
+      }
+      qf[kk] = __builtin_bit_cast(bf16x8, wq);
+      of[kk] = __builtin_bit_cast(bf16x8, wo);
+    }
+  }
+  constexpr float kLog2eF = 1.4426950408889634f;
+  const size_t stat = ((size_t)b * H + h) * T + (tq < T ? tq : 0);
+  const float l2 = a.lse[stat] * kLog2eF;
+  const float dd = a.dsum[stat];
+  f32x4 dq[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dq[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // keys of the workgroup and of this wave
+  const int wg_p_first = mb * BMP + off;
+  const int wg_p_last = min(mb * BMP + BMP, T) - 1 + off;
+  const int j_lo = a.is_local ? max(0, wg_p_first - win + 1) : 0;
+  const int n_start = (j_lo / BN) * BN;
+  const int n_tiles = (wg_p_last - n_start) / BN + 1;
+  const bool wave_active = t0 < T;
+  const int w_p_first = t0 + off;
+  const int w_p_last = min(t0 + 15, T - 1) + off;
+  const int w_j_lo = a.is_local ? max(0, w_p_first - win + 1) : 0;
+  const int w_j_lo_last = a.is_local ? max(0, w_p_last - win + 1) : 0;
+
+  const unsigned kv_row_bytes = (unsigned)KVH * D * 2u;
+  const char* kbase = reinterpret_cast<const char*>(a.k + ((size_t)b * S * KVH + g) * D);
+  const char* vbase = reinterpret_cast<const char*>(a.v + ((size_t)b * S * KVH + g) * D);
+  const unsigned dma_rl = lane >> 2;
+  const unsigned dma_lane = dma_rl * kv_row_bytes + (((lane & 3) ^ swz_rows(dma_rl)) * 16u);
+  auto issue = [&](char (*__restrict__ dst)[TILE], int n0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int n = wave + c * 4;
+      const int cg = n / RG, r0 = 16 * (n % RG);
+      const size_t uni = (size_t)(n0 + r0) * kv_row_bytes + 64u * cg;
+      const char* rk = kbase + uni;
+      const char* rv = vbase + uni;
+      unsigned lo = dma_lane;
+      asm volatile("" : "+s"(rk));
+      asm volatile("" : "+s"(rv));
+      asm volatile("" : "+v"(lo));
+      if (n0 + r0 + (int)dma_rl < S) {
+        __builtin_amdgcn_global_load_lds(rk + lo, G2B_LDS(&dst[0][n * 1024]), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(rv + lo, G2B_LDS(&dst[1][n * 1024]), 16, 0, 0);
+      }
+    }
+  };
+
+  const int k_lane = l16 * 64 + ((lq ^ swz_rows(l16)) << 4);
+  const int tr[2] = {tr_lane_off(l16, lq, 0), tr_lane_off(l16, lq, 1)};
+  const float k_in = a.cap.k_in, c_out = a.cap.c_out;
+  const float inv_cout = c_out > 0.f ? 1.0f / c_out : 0.f;
+  const float qs = a.query_scale;
+
+  auto compute = [&](const char (*__restrict__ buf)[TILE], int n0) __attribute__((always_inline)) {
+    if (!wave_active || n0 > w_p_last || n0 + BN - 1 < w_j_lo) return;
+    const bool need_mask = (n0 + BN - 1 > w_p_first) || (n0 + BN > S) ||
+                           (a.is_local && n0 < w_j_lo_last) || (t0 + 16 > T);
+    const char* kt = buf[0];
+    const char* vt = buf[1];
+    // S^T = K Q^T and dP^T = V dO^T: rows = keys (A from the tile), cols = queries
+    f32x4 st[2], dpt[2];
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + kk * (BN * 64) + kb * 1024 + k_lane);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vt + kk * (BN * 64) + kb * 1024 + k_lane);
+        st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[kk], kk == 0 ? zero4 : st[kb], 0, 0, 0);
+        dpt[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, of[kk], kk == 0 ? zero4 : dpt[kb], 0, 0, 0);
+      }
+    }
+    float dsv[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float s2 = capped<CAP>(st[kb][e], k_in, c_out);
+        const float p = exp2_fast(s2 - l2);
+        float ds = cap_grad<CAP>(p * (dpt[kb][e] - dd), s2, inv_cout, qs);
+        if (need_mask) {
+          const int j = n0 + 16 * kb + 4 * lq + e;
+          const int p_ = tq + off;
+          const bool vis = (tq < T) & (j < S) & (j <= p_) & ((j > p_ - win) | !a.is_local);
+          ds = vis ? ds : 0.f;
+        }
+        dsv[kb][e] = ds;
+      }
+    }
+    u32x4 w;
+    w[0] = pack_bf16x2(dsv[0][0], dsv[0][1]);
+    w[1] = pack_bf16x2(dsv[0][2], dsv[0][3]);
+    w[2] = pack_bf16x2(dsv[1][0], dsv[1][1]);
+    w[3] = pack_bf16x2(dsv[1][2], dsv[1][3]);
+    const bf16x8 sb = __builtin_bit_cast(bf16x8, w);
+    // dQ^T += K^T dS^T (k = the tile's 32 keys)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 kT = read_tr<BN>(kt, db, 0, tr);
+      dq[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kT, sb, dq[db], 0, 0, 0);
+    }
+  };
+
+  {
+    u32x4* z = reinterpret_cast<u32x4*>(&lds[0][0][0]);
+    for (int i = tid; i < (int)(sizeof(lds) / 16); i += 256) z[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  auto step = [&](const char (*__restrict__ cur)[TILE], char (*__restrict__ nxt)[TILE], int n0, bool more) __attribute__((always_inline)) {
+    if (more) issue(nxt, n0 + BN);
+    compute(cur, n0);
+  };
+  issue(lds[0], n_start);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int it = 0; it < n_tiles; it += 2) {
+    const int n0 = n_start + it * BN;
+    step(lds[0], lds[1], n0, it + 1 < n_tiles);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (it + 1 < n_tiles) {
+      step(lds[1], lds[0], n0 + BN, it + 2 < n_tiles);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  }
+
+  if (!wave_active || tq >= T) return;
+  bf16* qr = a.dq + (((size_t)b * T + tq) * H + h) * D + 4 * lq;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    u32x2 w2;
+    w2[0] = pack_bf16x2(dq[db][0], dq[db][1]);
+    w2[1] = pack_bf16x2(dq[db][2], dq[db][3]);
+    *reinterpret_cast<u32x2*>(qr + db * 16) = w2;
+  }
+}
+
+template <int D, int G, int CAP>
+static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+  const long rows = (long)a.B * a.T * a.H;
+  const unsigned gp = (unsigned)((rows * (D / 8) + 255) / 256);
+  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3(gp), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned nbg = (unsigned)(a.B * a.KVH);
+  const unsigned gk = (unsigned)((a.S + 63) / 64) * nbg;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, G, CAP>), dim3(gk), dim3(256), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int BMP = 16 * (4 / G);
+  const unsigned gq = (unsigned)((a.T + BMP - 1) / BMP) * nbg;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, G, CAP>), dim3(gq), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, int G>
+static hipError_t launch_bwd_dg(const BwdArgs& a, hipStream_t stream) {
+  switch (a.cap.mode) {
+    case kCapFast: return launch_bwd_t<D, G, kCapFast>(a, stream);
+    case kCapAccurate: return launch_bwd_t<D, G, kCapAccurate>(a, stream);
+    default: return launch_bwd_t<D, G, kCapNone>(a, stream);
+  }
+}
+
+hipError_t launch_prefill_backward(const BackwardLaunch& L, hipStream_t stream) {
+  BwdArgs a;
+  a.q = static_cast<const bf16*>(L.q);
+  a.k = static_cast<const bf16*>(L.k);
+  a.v = static_cast<const bf16*>(L.v);
+  a.out = static_cast<const bf16*>(L.out);
+  a.dout = static_cast<const bf16*>(L.dout);
+  a.lse = L.lse;
+  a.dsum = static_cast<float*>(L.workspace);
+  a.dq = static_cast<bf16*>(L.dq);
+  a.dk = static_cast<bf16*>(L.dk);
+  a.dv = static_cast<bf16*>(L.dv);
+  a.B = L.B;
+  a.T = L.T;
+  a.S = L.S;
+  a.H = L.H;
+  a.KVH = L.KVH;
+  a.cap = make_cap_consts(L.query_scale, L.softcap);
+  a.query_scale = L.query_scale;
+  a.window = L.window;
+  a.is_local = L.is_local;
+  const int G = L.H / L.KVH;
+  switch (L.d) {
+    case 64: return G == 2 ? launch_bwd_dg<64, 2>(a, stream) : launch_bwd_dg<64, 1>(a, stream);
+    case 128: return G == 2 ? launch_bwd_dg<128, 2>(a, stream) : launch_bwd_dg<128, 1>(a, stream);
+    case 256: return G == 2 ? launch_bwd_dg<256, 2>(a, stream) : launch_bwd_dg<256, 1>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace g2

@@ -54,6 +54,24 @@ inline int decode_call_splits(const DecodeLaunch& L) {
   return (int)((seen + kDecodeChunk - 1) / kDecodeChunk);
 }
 
+struct BackwardLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const void* dout;
+  const float* lse;  // (B, H, T) natural-log log-sum-exp from the forward
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, T, S, H, KVH, d;
+  float query_scale, softcap;
+  int window, is_local;
+  void* workspace;   // (B, H, T) fp32
+};
+
+hipError_t launch_prefill_backward(const BackwardLaunch& L, hipStream_t stream);
+
 struct RopeLaunch {
   void* x;                  // (B, T, NH, d), rotated in place
   const int32_t* positions;  // (B, T)

@@ -11,7 +11,10 @@ One step = the whole hot path on seeded synthetic inputs shaped like Gemma 2 9B:
   against its whole 8192-token cache (local and global).  The steps on either
   side of the attention call are timed after the steps, on their own: the
   rotary embedding of the 9B prefill's Q and K, and the final-logit soft-cap
-  (30) over the prefill batch's vocabulary logits (2*8192 x 256000, bf16).
+  (30) over the prefill batch's vocabulary logits (2*8192 x 256000, bf16);
+  and the backward pass of the 9B local+global pair (dq, dk, dv for a seeded
+  upstream gradient), counted as 10*d FLOPs per visible (query head, key) pair
+  (S recomputed, dP, dV, dK, dQ).
 
 Reported (one JSON line):
   value    prefill effective TFLOP/s = algorithmic FLOPs of the pair / prefill
@@ -146,6 +149,44 @@ def time_adjacent(g2, qd, kd, dev, stream, reps=10, vocab=256000):
                               "frac_of_hbm_peak": round(cap_bytes / t_cap / 1e9 / PEAK_HBM_GBS, 4),
                               "ms": round(t_cap * 1e3, 4), "bytes": cap_bytes,
                               "shape": [int(B * T), vocab]}}
+
+
+def time_backward(g2, qd, kd, vd, kw, dev, stream, reps=5):
+    """Backward pass of the local and global layer (after their forward with
+    log-sum-exp, outside the timed region)."""
+    import torch
+    from attention_g2attn_prefill_amd import synth
+    B, T, H, d = qd.shape
+    S = kd.shape[1]
+    dout = synth.draw(tuple(qd.shape), 17, 3).to(dev)
+    res = {}
+    total_f, total_t = 0.0, 0.0
+    for is_local in (True, False):
+        out, lse = g2.prefill_lse(qd, kd, vd, is_local=is_local, stream=stream, **kw)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        ws = torch.empty(B * H * T * 4, dtype=torch.uint8, device=dev)
+        g2.prefill_backward(qd, kd, vd, out, dout, lse, is_local=is_local, dq=dq, dk=dk, dv=dv,
+                            workspace=ws, stream=stream, **kw)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g2.prefill_backward(qd, kd, vd, out, dout, lse, is_local=is_local, dq=dq, dk=dk,
+                                dv=dv, workspace=ws, stream=stream, **kw)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / reps
+        f = 10.0 * d * B * H * prefill_pairs(T, S, kw["window"], is_local)
+        res["local" if is_local else "global"] = {"ms": round(t * 1e3, 4),
+                                                  "tflops": round(f / t / 1e12, 2)}
+        total_f += f
+        total_t += t
+        del out, lse, dq, dk, dv, ws
+    tf = total_f / total_t / 1e12
+    res.update({"metric": "backward eff. TFLOP/s (10*d per visible pair)", "value": round(tf, 2),
+                "unit": "TFLOP/s", "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                "executed_flops_per_pair": 14 * d, "flops": total_f})
+    return res
 
 
 def measured_traffic(src_hash, key="traffic_bytes_per_launch"):
@@ -357,6 +398,7 @@ def main():
     mn = ms.min(axis=0)
 
     adjacent = time_adjacent(g2, qd, kd, dev, stream, reps=10)
+    backward = time_backward(g2, qd, kd, vd, kw_p, dev, stream, reps=5)
     copy_rate = copy_gbs(dev)
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
@@ -446,6 +488,7 @@ def main():
         "decode": decode,
         "decode_paged": decode_paged,
         "adjacent": adjacent,
+        "backward": backward,
         "prefill_chunk": {"metric": "chunked prefill eff. TFLOP/s", "value": round(chunk_tflops, 2),
                           "unit": "TFLOP/s", "chunk": CT, "cache": S,
                           "frac_of_bf16_peak": round(chunk_tflops / PEAK_BF16_TFLOPS, 4),

@@ -93,6 +93,29 @@ int g2attn_prefill_lse(const void* q, const void* k, const void* v, void* out,
                        int is_local, int dtype, hipStream_t stream);
 
 /*
+ * Backward pass of the prefill (Gemma 2 Guide, "Deep Dive" item 1: the cap's
+ * derivative is 1 - tanh^2(x / cap)).  For an upstream gradient dout of the
+ * output it writes
+ *   dq (B,T,H,d), dk and dv (B,S,KVH,d): the gradients of the loss with
+ *   respect to q, k and v, summed over the query heads sharing a K/V head and
+ *   over every row that sees a key.
+ * q, k, v and the scalars are those of the forward call; out and lse are its
+ * results (g2attn_prefill_lse).  bf16 only (fp32: G2_ERR_UNSUPPORTED).
+ * workspace: device scratch of g2attn_prefill_backward_workspace_bytes(B,T,H)
+ * bytes (one float per row).  Buffers may not alias each other.
+ */
+int g2attn_prefill_backward(const void* q, const void* k, const void* v,
+                            const void* out, const void* dout, const float* lse,
+                            void* dq, void* dk, void* dv, int B, int T, int S,
+                            int H, int KVH, int d, float query_scale,
+                            float softcap, int window, int is_local, int dtype,
+                            void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/* Bytes of backward workspace for these sizes (0 for invalid sizes). */
+size_t g2attn_prefill_backward_workspace_bytes(int B, int T, int H);
+
+/*
  * Decode: one new query token per sequence against a KV cache of capacity S
  * (model card, "Method"; Guide section 2 on local layers keeping only the last
  * 4096 tokens).

@@ -25,7 +25,8 @@ def test_header_declares_the_entry_points():
     for n in ("g2attn_prefill", "g2attn_prefill_lse", "g2attn_decode", "g2attn_decode_workspace_bytes",
               "g2attn_check_args", "g2attn_status_string", "g2attn_decode_paged",
               "g2attn_decode_paged_workspace_bytes", "g2attn_check_paged_args",
-              "g2attn_rope", "g2attn_softcap"):
+              "g2attn_rope", "g2attn_softcap", "g2attn_prefill_backward",
+              "g2attn_prefill_backward_workspace_bytes"):
         assert n in names
 
 

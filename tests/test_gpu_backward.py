@@ -1,0 +1,129 @@
+"""GPU parity of the prefill backward pass (through the C ABI) against the
+fp64 oracle, which recomputes the gradients from q, k, v and dO alone (the GPU
+forward's out and lse are not trusted by the reference).
+
+Tolerances, relative to the size of each reference gradient: max |diff| <=
+2e-2 * max |ref| and mean |diff| <= 1e-2 * mean |ref|.  They follow from the
+arithmetic: P and dS are rounded to bf16 (2^-9 relative) before the MFMAs that
+build dV, dK and dQ, and the gradients are stored in bf16 (about 3e-3 of
+relative error together); D = <dO, out> is formed from the bf16 output, an
+error of about 2^-9 |D| that enters every dS_j = P_j (<dO, v_j> - D) of a row.
+Where a row's attention is nearly one-hot (saturated logits, or a row that sees
+few keys) the exact dS is far below that floor, so such rows' dq carries O(1)
+relative error at a tiny absolute size; it raises the mean ratio to ~7e-3 on
+the saturating case, hence the 1e-2 bound on the mean.  Gradients that are
+exactly zero by definition (a row that sees only itself: dq = dk = 0) keep the
+fp32 residue of <dO, v> - <dO, out> summed in two orders, so both bounds also
+allow 1e-4 absolute.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attention_g2attn_prefill_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+REL_MAX, REL_MEAN, ABS_FLOOR = 2e-2, 1e-2, 1e-4
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def g2():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import attention_g2attn_prefill_amd as mod
+    return mod
+
+
+def check_grad(got, ref, what):
+    got = np.asarray(got, np.float64)
+    assert got.shape == ref.shape
+    assert np.all(np.isfinite(got)), f"{what}: non-finite"
+    err = np.abs(got - ref)
+    scale_max, scale_mean = float(np.abs(ref).max()), float(np.abs(ref).mean())
+    if got.ndim == 4:  # where the error sits: per position, relative to that position's size
+        pe = err.mean(axis=(0, 2, 3)) / np.maximum(np.abs(ref).mean(axis=(0, 2, 3)), 1e-30)
+        worst = np.argsort(pe)[-5:][::-1]
+        say(f"{what}: worst positions {[(int(t), round(float(pe[t]), 4)) for t in worst]}")
+    say(f"{what}: max|d|/max|ref|={err.max() / max(scale_max, 1e-30):.3e} "
+        f"mean|d|/mean|ref|={err.mean() / max(scale_mean, 1e-30):.3e}")
+    assert err.max() <= REL_MAX * scale_max + ABS_FLOOR, what
+    assert err.mean() <= REL_MEAN * scale_mean + ABS_FLOOR, what
+
+
+def run_backward(g2, q, k, v, dout, kw):
+    qd, kd, vd, gd = q.cuda(), k.cuda(), v.cuda(), dout.cuda()
+    out, lse = g2.prefill_lse(qd, kd, vd, **kw)
+    dq, dk, dv = g2.prefill_backward(qd, kd, vd, out, gd, lse, **kw)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+BWD_CASES = [
+    # B, T, S, H, KVH, d, window, is_local, q_mul, softcap
+    (1, 200, 200, 4, 2, 256, 64, True, 3.0, 50.0),
+    (1, 200, 200, 4, 2, 256, 64, False, 3.0, 50.0),
+    (1, 300, 300, 4, 2, 128, 100, True, 3.0, 50.0),
+    (2, 150, 150, 2, 2, 64, 150, False, 2.0, 50.0),        # one query head per K/V head
+    (1, 100, 260, 4, 2, 256, 70, True, 3.0, 50.0),         # T < S
+    (1, 130, 130, 4, 2, 128, 40, True, 5.5, 50.0),         # saturating logits
+    (1, 120, 120, 4, 2, 256, 32, False, 2.0, 0.0),         # cap disabled
+    (1, 120, 120, 4, 2, 64, 32, True, 2.0, 1e6),           # accurate cap form
+    (1, 1, 1, 2, 1, 128, 1, True, 1.0, 50.0),              # one token
+    (1, 77, 77, 2, 1, 256, 1, True, 3.0, 50.0),            # window 1
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[f"bwd{i}" for i in range(len(BWD_CASES))])
+def test_backward_small(g2, case):
+    B, T, S, H, KVH, d, W, is_local, qm, cap = case
+    say(f"backward {case}")
+    seed = 800 + d + T
+    q = synth.draw((B, T, H, d), seed, 0, mul=qm)
+    k = synth.draw((B, S, KVH, d), seed, 1, mul=qm if qm > 4 else 1.0)
+    v = synth.draw((B, S, KVH, d), seed, 2)
+    dout = synth.draw((B, T, H, d), seed, 3)
+    kw = dict(query_scale=1 / np.sqrt(d), softcap=cap, window=W, is_local=is_local)
+    dq, dk, dv = run_backward(g2, q, k, v, dout, kw)
+    rq, rk, rv = oracle.prefill_backward(*(synth.to_f32_numpy(x) for x in (q, k, v, dout)), **kw)
+    check_grad(synth.to_f32_numpy(dq), rq, f"dq {case}")
+    check_grad(synth.to_f32_numpy(dk), rk, f"dk {case}")
+    check_grad(synth.to_f32_numpy(dv), rv, f"dv {case}")
+
+
+@pytest.mark.parametrize("is_local", [True, False], ids=["local", "global"])
+def test_backward_9b_heads_1k(g2, is_local):
+    """The 9B head layout (H=16, KVH=8, d=256) at 1024 positions, window 256."""
+    B, T, H, KVH, d, W = 1, 1024, 16, 8, 256, 256
+    say(f"backward 9b heads T={T} {'local' if is_local else 'global'}")
+    q = synth.draw((B, T, H, d), 901, 0, mul=3.0)
+    k = synth.draw((B, T, KVH, d), 901, 1, mul=3.0)
+    v = synth.draw((B, T, KVH, d), 901, 2)
+    dout = synth.draw((B, T, H, d), 901, 3)
+    kw = dict(query_scale=1 / 16, softcap=50.0, window=W, is_local=is_local)
+    dq, dk, dv = run_backward(g2, q, k, v, dout, kw)
+    rq, rk, rv = oracle.prefill_backward(*(synth.to_f32_numpy(x) for x in (q, k, v, dout)), **kw)
+    check_grad(synth.to_f32_numpy(dq), rq, "dq 9b-heads")
+    check_grad(synth.to_f32_numpy(dk), rk, "dk 9b-heads")
+    check_grad(synth.to_f32_numpy(dv), rv, "dv 9b-heads")
+
+
+def test_backward_deterministic(g2):
+    say("backward determinism")
+    q = synth.draw((1, 300, 4, 256), 911, 0, mul=3.0)
+    k = synth.draw((1, 300, 2, 256), 911, 1)
+    v = synth.draw((1, 300, 2, 256), 911, 2)
+    dout = synth.draw((1, 300, 4, 256), 911, 3)
+    kw = dict(query_scale=1 / 16, softcap=50.0, window=100, is_local=True)
+    a = run_backward(g2, q, k, v, dout, kw)
+    b = run_backward(g2, q, k, v, dout, kw)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
