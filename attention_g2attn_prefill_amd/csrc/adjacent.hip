@@ -13,6 +13,10 @@
 //
 // Final-logit soft-cap (Gemma 2 Guide, section 1, second formula): the
 // vocabulary logits become cap * tanh(x / cap) with cap = 30, in place.
+//
+// The logits are streamed once (non-temporal loads and stores); Q and K are
+// usually still in the caches from the projection that produced them, so the
+// rotary embedding uses ordinary accesses.
 #include "g2_device.h"
 #include "g2_kernels.h"
 
@@ -23,31 +27,40 @@ struct Lanes16;
 template <>
 struct Lanes16<bf16> {
   static constexpr int N = 8;
+  template <bool NT>
   __device__ static void load(const bf16* p, float (&v)[8]) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+    const u32x4* q = reinterpret_cast<const u32x4*>(p);
+    const u32x4 w = NT ? __builtin_nontemporal_load(q) : *q;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       v[2 * e] = bf16_lo_to_f32(w[e]);
       v[2 * e + 1] = bf16_hi_to_f32(w[e]);
     }
   }
+  template <bool NT>
   __device__ static void store(bf16* p, const float (&v)[8]) {
     u32x4 w;
 #pragma unroll
     for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
-    *reinterpret_cast<u32x4*>(p) = w;
+    if (NT) __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+    else *reinterpret_cast<u32x4*>(p) = w;
   }
 };
 template <>
 struct Lanes16<float> {
   static constexpr int N = 4;
+  template <bool NT>
   __device__ static void load(const float* p, float (&v)[4]) {
-    const f32x4 w = *reinterpret_cast<const f32x4*>(p);
+    const f32x4* q = reinterpret_cast<const f32x4*>(p);
+    const f32x4 w = NT ? __builtin_nontemporal_load(q) : *q;
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = w[e];
   }
+  template <bool NT>
   __device__ static void store(float* p, const float (&v)[4]) {
-    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+    const f32x4 w = {v[0], v[1], v[2], v[3]};
+    if (NT) __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(p));
+    else *reinterpret_cast<f32x4*>(p) = w;
   }
 };
 
@@ -74,16 +87,16 @@ __global__ __launch_bounds__(256) void rope_kernel(E* x, const int32_t* position
   E* row = x + (size_t)r * NH * D + i0;
   for (int h = 0; h < NH; ++h, row += D) {
     float a[N], b[N];
-    Lanes16<E>::load(row, a);
-    Lanes16<E>::load(row + HALF, b);
+    Lanes16<E>::template load<false>(row, a);
+    Lanes16<E>::template load<false>(row + HALF, b);
     float ya[N], yb[N];
 #pragma unroll
     for (int j = 0; j < N; ++j) {
       ya[j] = a[j] * c[j] - b[j] * s[j];
       yb[j] = b[j] * c[j] + a[j] * s[j];
     }
-    Lanes16<E>::store(row, ya);
-    Lanes16<E>::store(row + HALF, yb);
+    Lanes16<E>::template store<false>(row, ya);
+    Lanes16<E>::template store<false>(row + HALF, yb);
   }
 }
 
@@ -94,10 +107,10 @@ __global__ __launch_bounds__(256) void softcap_kernel(E* x, size_t n, float cap,
   const size_t stride = (size_t)gridDim.x * 256;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < nvec; i += stride) {
     float v[N];
-    Lanes16<E>::load(x + i * N, v);
+    Lanes16<E>::template load<true>(x + i * N, v);
 #pragma unroll
     for (int e = 0; e < N; ++e) v[e] = cap * tanhf(v[e] * inv_cap);
-    Lanes16<E>::store(x + i * N, v);
+    Lanes16<E>::template store<true>(x + i * N, v);
   }
   // tail: the last n % N elements, one thread each
   const size_t t = nvec * N + (size_t)blockIdx.x * 256 + threadIdx.x;

@@ -12,6 +12,8 @@
 //    (sequence, K/V head); both query heads of the pair reuse every K/V byte;
 //  * a key row is read by a group of d/8 lanes with 16-byte loads (d=256:
 //    half a wave per 512-byte row), so every load instruction is coalesced;
+//  * K/V rows are read once, with non-temporal loads, so the stream does not
+//    evict what other workgroups reuse from the caches;
 //  * each lane group keeps 4 keys' loads in flight and its own online-softmax
 //    state; logits are reduced across the group with lane shuffles;
 //  * groups, then waves (through LDS), are merged at the end, and each split
@@ -172,8 +174,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         slot = (size_t)sl;
       }
       if (pos < c1) {
-        kr[u] = *reinterpret_cast<const u32x4*>(kb + (size_t)slot * row_stride);
-        vr[u] = *reinterpret_cast<const u32x4*>(vb + (size_t)slot * row_stride);
+        kr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (size_t)slot * row_stride));
+        vr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + (size_t)slot * row_stride));
       } else {
         kr[u] = u32x4{0u, 0u, 0u, 0u};
         vr[u] = u32x4{0u, 0u, 0u, 0u};

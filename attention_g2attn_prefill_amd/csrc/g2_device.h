@@ -125,6 +125,16 @@ __device__ __forceinline__ float max_xor16_32(float v) {
 __device__ __forceinline__ float min_xor16_32(float v) {
   return reduce_xor16_32(v, [](float x, float y) { return fminf(x, y); });
 }
+// Min over the same lanes for values that are all >= +0 (or +inf): such floats
+// order like their bit patterns, so an unsigned min replaces the float min
+// and needs none of the NaN-quieting a float min of lane-swapped values gets.
+__device__ __forceinline__ float min_xor16_32_nonneg(float v) {
+  unsigned u = __builtin_bit_cast(unsigned, v);
+  auto a = __builtin_amdgcn_permlane16_swap(u, opaque_copy(u), false, false);
+  u = min((unsigned)a[0], (unsigned)a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(u, opaque_copy(u), false, false);
+  return __builtin_bit_cast(float, min((unsigned)b[0], (unsigned)b[1]));
+}
 __device__ __forceinline__ float sum_xor16_32(float v) {
   return reduce_xor16_32(v, [](float x, float y) { return x + y; });
 }

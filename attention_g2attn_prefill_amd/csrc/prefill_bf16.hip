@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
         for (int kb = 0; kb < P::kNB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) rmin = fminf(rmin, st[kb][qb][i]);
-        rmin = min_xor16_32(rmin);
+        rmin = min_xor16_32_nonneg(rmin);  // r is in [0, 1] or +inf (masked)
         mt = __builtin_fmaf(-2.0f * c_out, rmin, c_out);  // -inf when all masked
       } else {
         mt = kNegInf;
