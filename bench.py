@@ -208,7 +208,8 @@ def _counter_rows(path, counter):
     with open(path) as fh:
         for r in csv.DictReader(fh):
             if r["Counter_Name"] == counter:
-                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"]),
+                             int(r["Grid_Size"])))
     return sorted(rows)
 
 
@@ -221,28 +222,37 @@ def write_traffic(fetch_csv, write_csv, calib_mib):
     fetch = _counter_rows(fetch_csv, "FETCH_SIZE")
     write = _counter_rows(write_csv, "WRITE_SIZE")
     nbytes = calib_mib * 1024.0 * 1024.0
-    cf = max((v for _, n, v in fetch if "copyBuffer" in n), default=0.0)
-    cw = max((v for _, n, v in write if "copyBuffer" in n), default=0.0)
+    cf = max((v for _, n, v, _g in fetch if "copyBuffer" in n), default=0.0)
+    cw = max((v for _, n, v, _g in write if "copyBuffer" in n), default=0.0)
     if cf <= 0 or cw <= 0:
         raise SystemExit("no calibration copy found in the counter files")
     f_fetch = nbytes / (cf * 1024.0)
     f_write = nbytes / (cw * 1024.0)
 
-    def per_launch(tag):
-        fv = [v for _, n, v in fetch if tag in n]
-        wv = [v for _, n, v in write if tag in n]
+    def per_launch(tag, largest_grid=False):
+        """Mean over the dispatches of a kernel; with largest_grid, only those
+        of its largest grid (the full-size prefill, not the chunked one)."""
+        fs = [(v, g) for _, n, v, g in fetch if tag in n]
+        ws = [(v, g) for _, n, v, g in write if tag in n]
+        if largest_grid and fs and ws:
+            gmax = max(g for _, g in fs)
+            fs = [x for x in fs if x[1] == gmax]
+            ws = [x for x in ws if x[1] == gmax]
+        fv, wv = [v for v, _ in fs], [v for v, _ in ws]
         if not fv or not wv:
             return None
         return (sum(fv) / len(fv) * 1024.0 * f_fetch + sum(wv) / len(wv) * 1024.0 * f_write,
                 len(fv))
-    pre = per_launch("prefill_bf16_kernel")
-    dec = per_launch("decode_split_kernel")
+    pre = per_launch("prefill_bf16_kernel<256, 2, 32, 1>", largest_grid=True)
+    dec = per_launch("decode_split_kernelIDF16bLi256ELi2ELb0E")    # linear / ring cache
+    pag = per_launch("decode_split_kernelIDF16bLi256ELi2ELb1E")    # paged cache
     rec = {"source_sha256": kernel_source_hash(),
            "calibration_copy_mib": calib_mib,
            "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4),
            "traffic_bytes_per_launch": round(pre[0]) if pre else None,
            "prefill_launches": pre[1] if pre else 0,
            "decode_split_traffic_bytes_per_launch": round(dec[0]) if dec else None,
+           "paged_split_traffic_bytes_per_launch": round(pag[0]) if pag else None,
            "commands": [
                "rocprofv3 --pmc FETCH_SIZE -d <dir> -o p --output-format csv -- python3 bench.py "
                f"--steps 1 --warmup 1 --cpu-rows 0 --copy-calibration-mib {calib_mib}",
@@ -448,7 +458,8 @@ def main():
                     "block_size": PBS,
                     "roofline": {"bound": "hbm", "achieved": round(paged_gbs, 1),
                                  "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                 "frac": round(paged_gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                                 "frac": round(paged_gbs / PEAK_HBM_GBS, 4),
+                                 "traffic": measured_traffic(src_hash, "paged_split_traffic_bytes_per_launch")},
                     "ms_local": round(t_ql * 1e3, 4), "ms_global": round(t_qg * 1e3, 4),
                     "ms_local_median_min": [round(med[4], 4), round(mn[4], 4)],
                     "ms_global_median_min": [round(med[5], 4), round(mn[5], 4)]}
