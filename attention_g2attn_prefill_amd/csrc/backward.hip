@@ -25,8 +25,10 @@
 //    per wave) and streams 32-key tiles of K and V, like the forward:
 //    S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T.
 // Every tile uses one 16-byte-chunk swizzle, byte (c/4)*R*64 + r*64 +
-// 16*((c%4) ^ ((r/4)%4)) for chunk c of row r of an R-row tile: the row reads
-// are conflict-free; the transpose reads of the same tile share banks in part.
+// 16*((c%4) ^ sw(r)) for chunk c of row r of an R-row tile, with sw(r) the
+// two bits of (r/4)%4 swapped.  A 64-bank model shows both the row reads
+// (ds_read_b128) and the transpose reads (ds_read_b64_tr_b16) of such a tile
+// free of bank conflicts, so one layout serves both uses of Q, dO and K.
 #include "g2_device.h"
 #include "g2_kernels.h"
 
@@ -54,12 +56,13 @@ struct BwdArgs {
   int window, is_local;
 };
 
-__device__ __forceinline__ int swz_rows(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int swz_rows(int r) { return ((r >> 3) & 1) | (((r >> 2) & 1) << 1); }
 
 // Transpose-read lane offset inside an R-row tile for column block parity
-// `par`: lane reads row 4*lq + l16/4 at dims 16*db + 4*(l16%4).
+// `par`: lane reads row 4*lq + l16/4 at dims 16*db + 4*(l16%4) (rows 16 and
+// 32 further share the swizzle of row 4*lq).
 __device__ __forceinline__ int tr_lane_off(int l16, int lq, int par) {
-  return (4 * lq + (l16 >> 2)) * 64 + 16 * (((2 * par) + ((l16 & 3) >> 1)) ^ lq) + 8 * (l16 & 1);
+  return (4 * lq + (l16 >> 2)) * 64 + 16 * (((2 * par) + ((l16 & 3) >> 1)) ^ swz_rows(4 * lq)) + 8 * (l16 & 1);
 }
 
 // A-operand fragment of rows (tile rows 32*ks + 4*lq + j and + 16) x dims
@@ -246,15 +249,39 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     const float* lse_row = a.lse + ((size_t)b * H + h) * T;
     const float* d_row = a.dsum + ((size_t)b * H + h) * T;
     const int j = jw + l16;
+    // the 8 rows' log-sum-exp and D: 16-byte loads when the tile is whole and
+    // its rows start 16-byte aligned, else one clamped load per row
+    float lsev[2][4], dv4[2][4];
+    if (t0 + QT <= T && (T & 3) == 0) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_row + t0 + 16 * qb + 4 * lq);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(d_row + t0 + 16 * qb + 4 * lq);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lsev[qb][e] = l4[e];
+          dv4[qb][e] = d4[e];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = t0 + 16 * qb + 4 * lq + e;
+          const int tc = t < T ? t : T - 1;
+          lsev[qb][e] = lse_row[tc];
+          dv4[qb][e] = d_row[tc];
+        }
+    }
     float pv[2][4], dsv[2][4];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = t0 + 16 * qb + 4 * lq + e;
-        const int tc = t < T ? t : T - 1;
-        const float l2 = lse_row[tc] * kLog2eF;
-        const float dd = d_row[tc];
+        const float l2 = lsev[qb][e] * kLog2eF;
+        const float dd = dv4[qb][e];
         const float s2 = capped<CAP>(sc[qb][e], k_in, c_out);
         float p = exp2_fast(s2 - l2);
         float ds = cap_grad<CAP>(p * (dp[qb][e] - dd), s2, inv_cout, qs);
