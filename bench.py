@@ -60,11 +60,20 @@ def parse_args():
     return ap.parse_args()
 
 
-def kernel_source_hash():
+KERNEL_FILES = {  # the sources each measured kernel is built from
+    "prefill": ("prefill_bf16.hip", "g2_device.h", "g2_kernels.h"),
+    "decode": ("decode.hip", "g2_device.h", "g2_kernels.h"),
+}
+
+
+def kernel_source_hash(which=None):
+    """sha256 of the kernel sources (all of them, or those one kernel is built from)."""
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "attention_g2attn_prefill_amd", "csrc", "*"))):
-        with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode())
+    csrc = os.path.join(ROOT, "attention_g2attn_prefill_amd", "csrc")
+    names = KERNEL_FILES[which] if which else sorted(os.listdir(csrc))
+    for name in names:
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(name.encode())
             h.update(fh.read())
     return h.hexdigest()
 
@@ -189,15 +198,15 @@ def time_backward(g2, qd, kd, vd, kw, dev, stream, reps=5):
     return res
 
 
-def measured_traffic(src_hash, key="traffic_bytes_per_launch"):
+def measured_traffic(which, key):
     """HBM bytes per launch from committed counter runs, if they were taken on
-    the current kernel sources; else None."""
+    the current sources of that kernel; else None."""
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.loads(fh.read())
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != src_hash:
+    if rec.get(which + "_source_sha256") != kernel_source_hash(which):
         return None
     return rec.get(key)
 
@@ -246,7 +255,8 @@ def write_traffic(fetch_csv, write_csv, calib_mib):
     pre = per_launch("prefill_bf16_kernel<256, 2, 32, 1>", largest_grid=True)
     dec = per_launch("decode_split_kernelIDF16bLi256ELi2ELb0E")    # linear / ring cache
     pag = per_launch("decode_split_kernelIDF16bLi256ELi2ELb1E")    # paged cache
-    rec = {"source_sha256": kernel_source_hash(),
+    rec = {"prefill_source_sha256": kernel_source_hash("prefill"),
+           "decode_source_sha256": kernel_source_hash("decode"),
            "calibration_copy_mib": calib_mib,
            "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4),
            "traffic_bytes_per_launch": round(pre[0]) if pre else None,
@@ -439,7 +449,7 @@ def main():
     chunk_tflops = (fc_local + fc_global) / (t_cl + t_cg) / 1e12
 
     src_hash = kernel_source_hash()
-    traffic = measured_traffic(src_hash)
+    traffic = measured_traffic("prefill", "traffic_bytes_per_launch")
     roofline = {"bound": "mfma", "achieved": round(prefill_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(prefill_tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic}
@@ -448,7 +458,7 @@ def main():
               "roofline": {"bound": "hbm", "achieved": round(decode_gbs, 1),
                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "frac": round(decode_gbs / PEAK_HBM_GBS, 4),
-                           "traffic": measured_traffic(src_hash, "decode_split_traffic_bytes_per_launch")},
+                           "traffic": measured_traffic("decode", "decode_split_traffic_bytes_per_launch")},
               "ms_local": round(t_dl * 1e3, 4), "ms_global": round(t_dg * 1e3, 4),
               "ms_local_median_min": [round(med[2], 4), round(mn[2], 4)],
               "ms_global_median_min": [round(med[3], 4), round(mn[3], 4)],
@@ -459,7 +469,7 @@ def main():
                     "roofline": {"bound": "hbm", "achieved": round(paged_gbs, 1),
                                  "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                  "frac": round(paged_gbs / PEAK_HBM_GBS, 4),
-                                 "traffic": measured_traffic(src_hash, "paged_split_traffic_bytes_per_launch")},
+                                 "traffic": measured_traffic("decode", "paged_split_traffic_bytes_per_launch")},
                     "ms_local": round(t_ql * 1e3, 4), "ms_global": round(t_qg * 1e3, 4),
                     "ms_local_median_min": [round(med[4], 4), round(mn[4], 4)],
                     "ms_global_median_min": [round(med[5], 4), round(mn[5], 4)]}
