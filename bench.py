@@ -104,6 +104,25 @@ def prefill_tile_pairs(T, S, window, is_local, rows_per_wave=32, bn=32):
     return tot
 
 
+def gemm_tflops(dev, n=8192, reps=10):
+    """bf16 GEMM rate of torch's library path (n x n x n) on this GPU, for context:
+    the MFMA rate a tuned library reaches at the clock the chip holds under load."""
+    import torch
+    a = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
+    b = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
+    c = a @ b
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    secs = e0.elapsed_time(e1) * 1e-3 / reps
+    del a, b, c
+    return 2.0 * n ** 3 / secs / 1e12
+
+
 def copy_gbs(dev, mib=1024, reps=5):
     """Device-to-device copy rate (read + write bytes / time) on this GPU, for context."""
     import torch
@@ -420,6 +439,7 @@ def main():
     adjacent = time_adjacent(g2, qd, kd, dev, stream, reps=10)
     backward = time_backward(g2, qd, kd, vd, kw_p, dev, stream, reps=5)
     copy_rate = copy_gbs(dev)
+    gemm_rate = gemm_tflops(dev)
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -453,6 +473,8 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(prefill_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(prefill_tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic}
+    mfma_context = {"library_bf16_gemm_tflops": round(gemm_rate, 1), "gemm_shape": [8192, 8192, 8192],
+                    "prefill_frac_of_library_gemm": round(prefill_tflops / gemm_rate, 4)}
     decode = {"metric": "decode KV GB/s", "value": round(decode_gbs, 1), "unit": "GB/s",
               "frac_of_hbm_peak": round(decode_gbs / PEAK_HBM_GBS, 4),
               "roofline": {"bound": "hbm", "achieved": round(decode_gbs, 1),
@@ -506,6 +528,7 @@ def main():
                    "global_batch": B, "seq_len": T, "parallelism": "single-gpu"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "mfma_context": mfma_context,
         "decode": decode,
         "decode_paged": decode_paged,
         "adjacent": adjacent,
