@@ -304,3 +304,71 @@ def prefill_backward(q, k, v, dout, *, query_scale, softcap, window, is_local):
     if st != 0:
         raise OracleError(f"oracle rejected arguments (status {st})")
     return dq, dk, dv
+
+
+def prefill_backward_at(q, k, v, dout, out, lse, *, rows=(), keys=(), query_scale, softcap,
+                        window, is_local):
+    """Gradients of the prefill at chosen rows and keys, in float64.
+
+    Same definition as `prefill_backward` (Gemma 2 Guide, "Deep Dive" item 1,
+    the cap's derivative 1 - tanh^2; the model card's one-layer pseudocode for
+    the layer), evaluated only where asked, so that layers too large for the
+    full backward can be checked at sampled places.  Each row's weights come
+    from its capped logits and its log-sum-exp: w_j = exp(s_j - lse).
+
+    q, dout: (B,T,H,d); k, v: (B,S,KVH,d); out (B,T,H,d) and lse (B,T,H) are
+    the layer's output and natural-log log-sum-exp from this oracle's own
+    `prefill` and `prefill_lse` on the same inputs.  rows: (b, t, h) triples;
+    keys: (b, j, g) triples (g is the K/V head).  Returns (dq (len(rows), d),
+    dk (len(keys), d), dv (len(keys), d)).
+    """
+    q = _f32(q).astype(np.float64)
+    k = _f32(k).astype(np.float64)
+    v = _f32(v).astype(np.float64)
+    g = _f32(dout).astype(np.float64)
+    out = np.asarray(out, np.float64)
+    lse = np.asarray(lse, np.float64)
+    B, T, S, H, KVH, d = _shape_prefill(q, k, v)
+    if g.shape != q.shape or out.shape != q.shape or lse.shape != (B, T, H):
+        raise OracleError("dout/out must match q and lse must be (B, T, H)")
+    G = H // KVH
+    use_cap = softcap > 0 and np.isfinite(softcap)
+    off = S - T
+    dsum = np.einsum("bthe,bthe->bth", g, out)  # D = <dO, out> of every row
+
+    def sees(p, j):  # the mask of `allowed`, elementwise over arrays
+        ok = j <= p
+        if is_local:
+            ok &= j > p - window
+        return ok
+
+    def capped(x):  # capped logit s and the factor 1 - tanh^2 of dx = ds * factor
+        if not use_cap:
+            return x, np.ones_like(x)
+        th = np.tanh(x / softcap)
+        return softcap * th, 1.0 - th * th
+
+    dq = np.zeros((len(rows), d))
+    for n, (b, t, h) in enumerate(rows):
+        kg, vg = k[b, :, h // G], v[b, :, h // G]                    # (S, d)
+        x = query_scale * (kg @ q[b, t, h])
+        s, fac = capped(x)
+        js = np.arange(S)
+        w = np.where(sees(t + off, js), np.exp(s - lse[b, t, h]), 0.0)
+        ds = w * (vg @ g[b, t, h] - dsum[b, t, h])
+        dq[n] = query_scale * ((ds * fac) @ kg)
+
+    dk = np.zeros((len(keys), d))
+    dv = np.zeros((len(keys), d))
+    ts = np.arange(T)
+    for n, (b, j, gh) in enumerate(keys):
+        vis = sees(ts + off, j)
+        for h in range(gh * G, gh * G + G):
+            qh, gr = q[b, :, h], g[b, :, h]                            # (T, d)
+            x = query_scale * (qh @ k[b, j, gh])
+            s, fac = capped(x)
+            w = np.where(vis, np.exp(s - lse[b, :, h]), 0.0)
+            ds = w * (gr @ v[b, j, gh] - dsum[b, :, h])
+            dk[n] += query_scale * ((ds * fac) @ qh)
+            dv[n] += w @ gr
+    return dq, dk, dv

@@ -127,3 +127,60 @@ def test_backward_deterministic(g2):
     b = run_backward(g2, q, k, v, dout, kw)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("is_local", [True, False], ids=["local", "global"])
+def test_backward_9b_8k_sampled(g2, is_local):
+    """The 9B layer at full size, in the launch configuration the benchmark
+    times (B=2, T=S=8192, H=16, KVH=8, d=256, window 4096).  Two (batch, K/V
+    head) groups, one at each end of the grid, are checked at sampled query
+    rows (dq) and keys (dk, dv) against the oracle, whose forward out and lse
+    come from the oracle itself on that group's slice (groups are independent).
+    Over every key, dv summed per group must equal the group's upstream
+    gradient summed over rows and heads (each row's weights sum to 1)."""
+    cfg = synth.WORKLOADS["9b-8k"]
+    q, k, v = synth.prefill_inputs(cfg)
+    dout = synth.draw(tuple(q.shape), 17, 3)
+    B, T, H, d = q.shape
+    S, KVH = k.shape[1], k.shape[2]
+    G, W = H // KVH, cfg["window"]
+    kw = dict(query_scale=cfg["query_scale"], softcap=cfg["softcap"], window=W, is_local=is_local)
+    say(f"backward full 9b-8k {'local' if is_local else 'global'}")
+    dq, dk, dv = run_backward(g2, q, k, v, dout, kw)
+    dqn, dkn, dvn = (synth.to_f32_numpy(x).astype(np.float64) for x in (dq, dk, dv))
+    assert np.all(np.isfinite(dqn)) and np.all(np.isfinite(dkn)) and np.all(np.isfinite(dvn))
+
+    # every key: sum of dv over keys == sum of dO over the group's rows and heads.
+    # The weights enter dv rounded to bf16; a peaky row's top weight sits just
+    # below 1, where the bf16 step is 2^-8, so each row's weights sum to 1 only
+    # within about 2^-9.  Against the row's dO that gives an error of standard
+    # deviation <= 2^-9 * sqrt(sum over the group's rows of dO^2) per element
+    # (~0.25 here, |sum| ~ 100); the bound is five of those.
+    g64 = synth.to_f32_numpy(dout).astype(np.float64).reshape(B, T, KVH, G, d)
+    want = g64.sum(axis=(1, 3))
+    bound = 5 * 2.0 ** -9 * np.sqrt((g64 ** 2).sum(axis=(1, 3)))
+    got = dvn.sum(axis=1)
+    err = np.abs(got - want)
+    say(f"sum dv over keys: max|d|={err.max():.3e}, max |d|/bound={np.max(err / bound):.3f}")
+    assert np.all(err <= bound)
+
+    rng = np.random.default_rng(41)
+    ts = sorted({0, 1, 31, 32, 63, W - 1, W, W + 1, T - 33, T - 1, *rng.integers(0, T, 6).tolist()})
+    js = sorted({0, 1, 15, 16, 63, 64, W - 1, W, T - 65, T - 64, T - 2, T - 1,
+                 *rng.integers(0, S, 6).tolist()})
+    for b, g in ((0, 0), (B - 1, KVH - 1)):
+        hs = slice(g * G, g * G + G)
+        qn = synth.to_f32_numpy(q[b:b + 1, :, hs])
+        kn = synth.to_f32_numpy(k[b:b + 1, :, g:g + 1])
+        vn = synth.to_f32_numpy(v[b:b + 1, :, g:g + 1])
+        gn = synth.to_f32_numpy(dout[b:b + 1, :, hs])
+        out = oracle.prefill(qn, kn, vn, **kw)
+        lse = oracle.prefill_lse(qn, kn, **kw)
+        rows = [(0, t, hh) for t in ts for hh in range(G)]
+        keys = [(0, j, 0) for j in js]
+        rq, rk, rv = oracle.prefill_backward_at(qn, kn, vn, gn, out, lse, rows=rows, keys=keys,
+                                                **kw)
+        got_q = np.stack([dqn[b, t, g * G + hh] for (_, t, hh) in rows])
+        check_grad(got_q, rq, f"dq rows of group ({b},{g})")
+        check_grad(dkn[b, js, g], rk, f"dk keys of group ({b},{g})")
+        check_grad(dvn[b, js, g], rv, f"dv keys of group ({b},{g})")

@@ -716,3 +716,71 @@ def test_backward_window_one_closed_form():
     assert np.max(np.abs(dq)) <= 1e-15 and np.max(np.abs(dk)) <= 1e-15
     want = R.astype(np.float64).reshape(B, T, KVH, H // KVH, d).sum(axis=3)
     assert np.max(np.abs(dv - want)) <= 1e-14
+
+
+# ---- gradients at sampled rows and keys (used where the full backward is too slow)
+
+@pytest.mark.parametrize("B,T,S,H,KVH,d,window,is_local,cap", [
+    (2, 40, 55, 4, 2, 16, 12, True, 50.0),    # T < S, local
+    (1, 33, 33, 2, 1, 8, 33, False, 0.0),     # cap disabled
+    (1, 30, 30, 4, 2, 8, 5, True, 1e6),       # accurate cap range
+    (1, 20, 20, 4, 4, 8, 1, True, 5.0),       # window 1, one query head per K/V head
+])
+def test_backward_at_equals_full_backward(B, T, S, H, KVH, d, window, is_local, cap):
+    """At every row and key, the sampled routine equals the full backward."""
+    q, k, v, R = (rand((B, T, H, d), 311, mul=3.0), rand((B, S, KVH, d), 312, mul=3.0),
+                  rand((B, S, KVH, d), 313), rand((B, T, H, d), 314))
+    kw = dict(query_scale=0.3, softcap=cap, window=window, is_local=is_local)
+    dq, dk, dv = oracle.prefill_backward(q, k, v, R, **kw)
+    out, lse = oracle.prefill(q, k, v, **kw), oracle.prefill_lse(q, k, **kw)
+    rows = [(b, t, h) for b in range(B) for t in range(T) for h in range(H)]
+    keys = [(b, j, g) for b in range(B) for j in range(S) for g in range(KVH)]
+    sq, sk, sv = oracle.prefill_backward_at(q, k, v, R, out, lse, rows=rows, keys=keys, **kw)
+    for got, ref in ((sq, dq), (sk, dk), (sv, dv)):
+        ref = ref.reshape(got.shape)
+        assert np.max(np.abs(got - ref)) <= 1e-12 * (1.0 + np.max(np.abs(ref)))
+
+
+def test_backward_at_matches_central_differences():
+    """Sampled gradient entries against central differences of the forward
+    oracle, step 2^-12 on grid inputs (independent of the full backward)."""
+    B, T, S, H, KVH, d = 1, 7, 9, 4, 2, 4
+    q, k, v, R = _grid_case(321, B, T, S, H, KVH, d)
+    kw = dict(query_scale=0.5, softcap=5.0, window=4, is_local=True)
+    out, lse = oracle.prefill(q, k, v, **kw), oracle.prefill_lse(q, k, **kw)
+    rows, keys = [(0, 6, 1), (0, 3, 2)], [(0, 2, 0), (0, 8, 1)]
+    sq, sk, sv = oracle.prefill_backward_at(q, k, v, R, out, lse, rows=rows, keys=keys, **kw)
+    h = 2.0 ** -12
+    R64 = R.astype(np.float64)
+
+    def fd(arr, idx, which):
+        plus, minus = arr.copy(), arr.copy()
+        plus[idx] += np.float32(h)
+        minus[idx] -= np.float32(h)
+        args = lambda a: tuple(a if n == which else x for n, x in (("q", q), ("k", k), ("v", v)))
+        lp = np.sum(oracle.prefill(*args(plus), **kw) * R64)
+        lm = np.sum(oracle.prefill(*args(minus), **kw) * R64)
+        return (lp - lm) / (2 * h)
+
+    for n, (b, t, hh) in enumerate(rows):
+        for e in range(d):
+            want = fd(q, (b, t, hh, e), "q")
+            assert abs(want - sq[n, e]) <= 1e-6 * (1.0 + abs(want))
+    for n, (b, j, g) in enumerate(keys):
+        for e in range(d):
+            want_k, want_v = fd(k, (b, j, g, e), "k"), fd(v, (b, j, g, e), "v")
+            assert abs(want_k - sk[n, e]) <= 1e-6 * (1.0 + abs(want_k))
+            assert abs(want_v - sv[n, e]) <= 1e-6 * (1.0 + abs(want_v))
+
+
+def test_backward_dv_sums_to_upstream_gradient():
+    """Each row's weights sum to 1, so summed over every key of a group, dv
+    equals the sum of that group's upstream gradients over rows and heads."""
+    B, T, S, H, KVH, d = 2, 30, 36, 4, 2, 8
+    q, k, v, R = (rand((B, T, H, d), 331, mul=3.0), rand((B, S, KVH, d), 332),
+                  rand((B, S, KVH, d), 333), rand((B, T, H, d), 334))
+    for is_local, window in ((True, 5), (False, 36)):
+        _, _, dv = oracle.prefill_backward(q, k, v, R, query_scale=0.4, softcap=50.0,
+                                           window=window, is_local=is_local)
+        want = R.astype(np.float64).reshape(B, T, KVH, H // KVH, d).sum(axis=(1, 3))
+        assert np.max(np.abs(dv.sum(axis=1) - want)) <= 1e-12
