@@ -137,3 +137,59 @@ def test_final_softcap_disabled_leaves_data(g2):
         g2.softcap_(y, cap)
     torch.cuda.synchronize()
     assert torch.equal(x, y)
+
+
+# ---------------------------------------------- the sizes the benchmark times
+
+def test_rope_9b_full_size_sampled(g2):
+    """Q of the 9B layer (B=2, T=8192, 16 heads, d=256) at positions 0..T-1,
+    in place as the benchmark runs it; sampled rows against the oracle."""
+    cfg = synth.WORKLOADS["9b-8k"]
+    B, T, H, d = cfg["B"], cfg["T"], cfg["H"], cfg["d"]
+    say("rope full 9b q")
+    q, _, _ = synth.prefill_inputs(cfg)
+    pos = torch.arange(T, dtype=torch.int32).repeat(B, 1).contiguous()
+    qd = q.cuda()
+    g2.rope_(qd, pos.cuda())
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(51)
+    ts = sorted({0, 1, 2, 255, 4095, 4096, T - 2, T - 1, *rng.integers(0, T, 40).tolist()})
+    for b in range(B):
+        xs = synth.to_f32_numpy(q[b:b + 1, ts])                   # (1, n, H, d)
+        ps = np.asarray(ts, np.int32).reshape(1, -1)
+        ref = oracle.rope(xs, ps)
+        got = synth.to_f32_numpy(qd[b:b + 1, ts].cpu())
+        xn = xs.astype(np.float64)
+        h = d // 2
+        pair = np.abs(xn[..., :h]) + np.abs(xn[..., h:])
+        arith = 4.0 * 2.0 ** -24 * np.concatenate([pair, pair], axis=-1)
+        check_storage(got, ref, "bf16", f"rope full 9b batch {b}", arith=arith)
+
+
+def test_final_softcap_full_size_sampled(g2):
+    """The final cap (30) over the 9B batch's logits, 16384 x 256000 bf16
+    (4.19e9 elements, so offsets pass 2^31), in place.  Inputs come from a
+    seeded generator on the device; sampled elements, among them the first
+    and last ones and both sides of 2^31, are read before and after the call
+    and checked against the oracle; every element must lie within the cap."""
+    rows, vocab = 16384, 256000
+    n = rows * vocab
+    say("final soft-cap full 16384 x 256000")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(61)
+    x = torch.randn((rows, vocab), generator=gen, device="cuda", dtype=torch.float32).mul_(15.0)
+    x = x.to(torch.bfloat16)
+    flat = x.view(-1)
+    rng = np.random.default_rng(62)
+    idx = np.unique(np.concatenate([
+        np.array([0, 1, 7, 8, 2 ** 31 - 9, 2 ** 31 - 1, 2 ** 31, 2 ** 31 + 8, n - 9, n - 1]),
+        rng.integers(0, n, 20000)])).astype(np.int64)
+    it = torch.from_numpy(idx).cuda()
+    before = synth.to_f32_numpy(flat.index_select(0, it).cpu())
+    g2.softcap_(x, 30.0)
+    torch.cuda.synchronize()
+    assert float(flat.abs().max()) <= 30.0
+    got = synth.to_f32_numpy(flat.index_select(0, it).cpu())
+    ref = oracle.softcap_array(before, 30.0)
+    check_storage(got, ref, "bf16", f"soft-cap full ({idx.size} sampled elements)")
+    del x, flat
