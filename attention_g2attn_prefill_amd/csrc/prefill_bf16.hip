@@ -25,11 +25,17 @@
 //    from registers.  The V^T operand comes from the row-major V tile through
 //    the LDS transpose read (ds_read_b64_tr_b16): within each 16-lane group,
 //    lane 4a+c receives element c of the rows read by lanes a, a+4, a+8, a+12.
-//  * Soft-cap, mask and online softmax run in fp32 in base 2.  With the fast
-//    cap form s = C - 2C*r, r = 1/(1+e^{2y}), the row max is taken on r (a
-//    min) and p = 2^(fma(r, -2C, C - m)), one VALU op less per logit.  The
-//    running max is rescaled lazily: O and l are multiplied down only when a
-//    row's max grows by more than 8 (log2 units).
+//  * Soft-cap, mask and softmax run in fp32 in base 2.  With the fast cap form
+//    s = C - 2C*r, r = 1/(1+e^{2y}), a weight is p = 2^(fma(r, -2C, C - m)).
+//    The cap bounds every logit to [-C, C], so for caps up to ~55 one constant
+//    offset m serves every row (no running max, no rescaling, no row
+//    reductions); larger caps and the uncapped layer keep a running max,
+//    rescaled lazily: O and l are multiplied down only when a row's max grows
+//    by more than 8 (log2 units).
+//  * Each row's normaliser is the sum of the bf16 weights that multiply V,
+//    formed by one more MFMA against a ones operand, so the weights the output
+//    uses sum to exactly one: a dominant weight's bf16 rounding cancels instead
+//    of scaling the whole row.  The log-sum-exp output keeps an exact fp32 sum.
 //  * Tiles wholly outside the causal / sliding-window band are skipped; the
 //    mask is evaluated only on tiles that cross the band's edges.
 //  * Work order: heaviest query blocks first; consecutive workgroups take
@@ -82,10 +88,20 @@ struct PrefillArgs {
   int window;
   int is_local;
   int n_mblocks;
+  float m_fixed;  // FIXED kernels: the constant softmax offset M (log2 units)
 };
 
-template <int D, int G, int BN, int CAP>
+// Softmax offset for caps small enough that one constant serves every row:
+// capped logits lie in [-C, C] (C = cap*log2 e), so with weights 2^(s - M),
+// M = 110 - C, a row's largest weight is at least 2^-110 (normal fp32 and
+// bf16) and no weight exceeds 2^(2C - 110) <= 2^50; l and O then stay below
+// 2^81 * max|v| for any 2^31 keys.  No running max, no rescaling.
+constexpr float kFixedOffsetMaxC = 80.0f;
+constexpr float kFixedOffsetLow = 110.0f;
+
+template <int D, int G, int BN, int CAP, bool FIXED, bool LSE>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
+  static_assert(!FIXED || CAP == kCapFast, "the constant offset needs the bounded fast cap");
   using P = PrefillShape<D, G, BN>;
   constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
   // [buffer][K|V] tiles, each BN rows of D bf16, rows stored whole and swizzled
@@ -181,8 +197,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   for (int db = 0; db < P::kDB; ++db)
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {kNegInf, kNegInf};
-  float l_run[2] = {0.f, 0.f};
+  float m_run[2] = {FIXED ? a.m_fixed : kNegInf, FIXED ? a.m_fixed : kNegInf};
+  float l_run[2] = {0.f, 0.f};  // exact fp32 row sums, kept only for the log-sum-exp output
+  // Row sums of the bf16 weights that multiply V, by MFMA against a ones
+  // operand: every element of lsum[qb] in every lane is the sum of its query
+  // column, so the output is normalised by exactly the weights it used.
+  f32x4 lsum[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
   const float k_in = a.cap.k_in, c_out = a.cap.c_out;
   const int win = a.window;
 
@@ -247,9 +268,27 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
           for (int i = 0; i < 4; ++i) st[kb][qb][i] = cap_of(st[kb][qb][i]);
     }
 
+    // ---- softmax weights with the constant offset (bounded cap)
+    if constexpr (FIXED) {
+      const float base = c_out - a.m_fixed;
+      const float slope = -2.0f * c_out;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        float ls = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < P::kNB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = exp2_fast(__builtin_fmaf(st[kb][qb][i], slope, base));
+            st[kb][qb][i] = p;
+            if constexpr (LSE) ls += p;
+          }
+        if constexpr (LSE) l_run[qb] += ls;
+      }
+    }
     // ---- online softmax (per lane: two query columns)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < (FIXED ? 0 : 2); ++qb) {
       float mt;
       if constexpr (CAP == kCapFast) {
         float rmin = __builtin_inff();
@@ -273,6 +312,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
         const float alpha = grow ? exp2_fast(m_run[qb] - m_new) : 1.0f;
         m_run[qb] = m_new;
         l_run[qb] *= alpha;
+        lsum[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < P::kDB; ++db) o[db][qb] *= alpha;
       }
@@ -287,7 +327,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
           for (int i = 0; i < 4; ++i) {
             const float p = exp2_fast(__builtin_fmaf(st[kb][qb][i], slope, base));
             st[kb][qb][i] = p;
-            ls += p;
+            if constexpr (LSE) ls += p;
           }
       } else {
 #pragma unroll
@@ -296,10 +336,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
           for (int i = 0; i < 4; ++i) {
             const float p = exp2_fast(st[kb][qb][i] - m_use);
             st[kb][qb][i] = p;
-            ls += p;
+            if constexpr (LSE) ls += p;
           }
       }
-      l_run[qb] += ls;
+      if constexpr (LSE) l_run[qb] += ls;
     }
 
     // ---- O^T += V^T * P^T; V^T operand rows (keys) 32*ks + 4*lq + j and
@@ -315,6 +355,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
         w[2] = pack_bf16x2(st[2 * ks + 1][qb][0], st[2 * ks + 1][qb][1]);
         w[3] = pack_bf16x2(st[2 * ks + 1][qb][2], st[2 * ks + 1][qb][3]);
         pf[qb] = __builtin_bit_cast(bf16x8, w);
+        lsum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qb], lsum[qb], 0, 0, 0);
       }
       auto read_v = [&](int db) __attribute__((always_inline)) {
         const char* vb = vt + (db >> 1) * (BN * 64) + (32 * ks) * 64 + ((db & 1) ? v_lane1 : v_lane0);
@@ -370,12 +411,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   // ---- epilogue: O = O^T / l, bf16, store 4 consecutive dims per lane and block
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float lt = sum_xor16_32(l_run[qb]);
-    const float inv = 1.0f / lt;
+    const float inv = 1.0f / lsum[qb][0];
     const int t = t0 + qb * 16 + l16;
     // l and O are kept relative to 2^m_run (log2 units of the capped logit)
-    if (a.lse && lq == 0 && t < T)
-      a.lse[((size_t)b * H + h) * T + t] = (m_run[qb] + __log2f(lt)) * 0.69314718055994531f;
+    if constexpr (LSE) {
+      const float lt = sum_xor16_32(l_run[qb]);
+      if (lq == 0 && t < T)
+        a.lse[((size_t)b * H + h) * T + t] = (m_run[qb] + __log2f(lt)) * 0.69314718055994531f;
+    }
     if (t < T) {
       bf16* orow = a.out + (((size_t)b * T + t) * H + h) * D + lq * 4;
 #pragma unroll
@@ -389,11 +432,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   }
 }
 
-template <int D, int G, int BN, int CAP>
+template <int D, int G, int BN, int CAP, bool FIXED = false>
 static hipError_t launch_prefill_bf16_t(const PrefillArgs& a, int B, hipStream_t stream) {
   using P = PrefillShape<D, G, BN>;
   const unsigned grid = (unsigned)a.n_mblocks * (unsigned)(B * a.KVH);
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, G, BN, CAP>), dim3(grid), dim3(P::kThreads), 0, stream, a);
+  if (a.lse)
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, G, BN, CAP, FIXED, true>), dim3(grid), dim3(P::kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, G, BN, CAP, FIXED, false>), dim3(grid), dim3(P::kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -402,7 +448,12 @@ static hipError_t launch_prefill_bf16_dg(PrefillArgs a, const PrefillLaunch& L, 
   using P = PrefillShape<D, G, BN>;
   a.n_mblocks = (L.T + P::kBMP - 1) / P::kBMP;
   switch (a.cap.mode) {
-    case kCapFast: return launch_prefill_bf16_t<D, G, BN, kCapFast>(a, L.B, stream);
+    case kCapFast:
+      if (a.cap.c_out <= kFixedOffsetMaxC) {
+        a.m_fixed = kFixedOffsetLow - a.cap.c_out;
+        return launch_prefill_bf16_t<D, G, BN, kCapFast, true>(a, L.B, stream);
+      }
+      return launch_prefill_bf16_t<D, G, BN, kCapFast>(a, L.B, stream);
     case kCapAccurate: return launch_prefill_bf16_t<D, G, BN, kCapAccurate>(a, L.B, stream);
     default: return launch_prefill_bf16_t<D, G, BN, kCapNone>(a, L.B, stream);
   }
@@ -423,6 +474,7 @@ hipError_t launch_prefill_bf16(const PrefillLaunch& L, hipStream_t stream) {
   a.window = L.window;
   a.is_local = L.is_local;
   a.n_mblocks = 0;
+  a.m_fixed = 0.0f;
   const int G = L.H / L.KVH;
   switch (L.d) {
     case 64:

@@ -106,12 +106,39 @@ def test_prefill_uncapped_and_large_cap(g2):
     k = synth.draw((B, T, KVH, d), 7, 1)
     v = synth.draw((B, T, KVH, d), 7, 2)
     qn, kn, vn = (synth.to_f32_numpy(x) for x in (q, k, v))
-    for cap in (0.0, float("inf"), 1e6):
+    # 30, 50, 55: the constant-offset softmax; 56, 200: the fast cap with a
+    # running max; 1e6: the accurate cap form; 0 and inf: no cap
+    for cap in (0.0, float("inf"), 1e6, 30.0, 50.0, 55.0, 56.0, 200.0):
         out = g2.prefill(q.cuda(), k.cuda(), v.cuda(), query_scale=0.1, softcap=cap, window=40,
                          is_local=True)
         torch.cuda.synchronize()
         ref = oracle.prefill(qn, kn, vn, query_scale=0.1, softcap=cap, window=40, is_local=True)
         check(synth.to_f32_numpy(out), ref, "bf16", f"cap={cap}")
+
+
+@pytest.mark.parametrize("cap", [50.0, 55.0, 56.0])
+@pytest.mark.parametrize("sign", [-1.0, 1.0], ids=["low", "high"])
+def test_prefill_rows_saturated_at_the_cap(g2, cap, sign):
+    """Every key equal to sign * (a large multiple of) the one query direction:
+    all logits saturate at +-cap, every visible key has the same weight, and
+    each output row is the mean of the value rows it sees (the smallest and the
+    largest weights the constant softmax offset must represent)."""
+    say(f"prefill saturated rows cap={cap} sign={sign}")
+    B, T, H, KVH, d, W = 1, 150, 2, 1, 128, 40
+    u = np.zeros(d, np.float32)
+    u[::3] = 1.0
+    q = torch.from_numpy(np.broadcast_to(u * 4.0, (B, T, H, d)).copy()).to(torch.bfloat16)
+    k = torch.from_numpy(np.broadcast_to(u * (sign * 4.0), (B, T, KVH, d)).copy()).to(torch.bfloat16)
+    v = synth.draw((B, T, KVH, d), 41, 2)
+    vn = synth.to_f32_numpy(v).astype(np.float64)
+    for is_local in (True, False):
+        out = g2.prefill(q.cuda(), k.cuda(), v.cuda(), query_scale=1.0, softcap=cap, window=W,
+                         is_local=is_local)
+        torch.cuda.synchronize()
+        lo = lambda t: max(0, t - W + 1) if is_local else 0
+        want = np.stack([vn[0, lo(t):t + 1, 0].mean(axis=0) for t in range(T)])
+        want = np.broadcast_to(want[None, :, None, :], (B, T, H, d))
+        check(synth.to_f32_numpy(out), want, "bf16", f"saturated cap={cap} sign={sign}")
 
 
 # ------------------------------------------------------- full-size prefill
