@@ -271,7 +271,7 @@ def write_traffic(fetch_csv, write_csv, calib_mib):
             return None
         return (sum(fv) / len(fv) * 1024.0 * f_fetch + sum(wv) / len(wv) * 1024.0 * f_write,
                 len(fv))
-    pre = per_launch("prefill_bf16_kernel<256, 2, 32, 1>", largest_grid=True)
+    pre = per_launch("prefill_bf16_kernel<256, 2, 32, 1, true, false>", largest_grid=True)  # cap 50: constant offset, no lse
     dec = per_launch("decode_split_kernelIDF16bLi256ELi2ELb0E")    # linear / ring cache
     pag = per_launch("decode_split_kernelIDF16bLi256ELi2ELb1E")    # paged cache
     rec = {"prefill_source_sha256": kernel_source_hash("prefill"),
