@@ -76,24 +76,34 @@ __device__ __forceinline__ bf16x8 read_tr(const char* tile, int db, int ks, cons
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Gradient of the capped logit with respect to the raw score <q, k>, times
-// the softmax term: dS * (1 - tanh^2) * qs, from the capped logit s2 in log2
-// units (tanh = s2 / (cap log2 e)).
+// The two per-score factors of the backward for raw score x = <q, k>:
+//   p = exp(s - lse) = 2^(s2 - l2), s2 the capped logit in log2 units;
+//   g = the cap's derivative 1 - tanh^2 up to a constant, so that
+//   dx = p (<dO, v> - D) * g * grad_scale<CAP>(qs).
+// Fast form: s2 = C (1 - 2r) with r = 1/(1 + e^{2y}), so tanh = 1 - 2r and
+// 1 - tanh^2 = 4 r (1 - r): g = r (1 - r) in one fma, and 4 qs is applied
+// to the accumulated gradient.  row is C - l2 for the fast form, -l2 else.
 template <int CAP>
-__device__ __forceinline__ float cap_grad(float ds, float s2, float inv_cout, float qs) {
-  if constexpr (CAP == kCapNone) {
-    return ds * qs;
-  } else {
+__device__ __forceinline__ float2 score_terms(float x, float k_in, float c_out, float inv_cout, float row) {
+  if constexpr (CAP == kCapFast) {
+    const float r = rcp_fast(1.0f + exp2_fast(x * k_in));
+    return float2{exp2_fast(__builtin_fmaf(r, -2.0f * c_out, row)), __builtin_fmaf(-r, r, r)};
+  } else if constexpr (CAP == kCapAccurate) {
+    const float s2 = capped_log2_accurate(x, k_in, c_out);
     const float t = s2 * inv_cout;
-    return ds * ((1.0f - t) * (1.0f + t)) * qs;
+    return float2{exp2_fast(s2 + row), __builtin_fmaf(-t, t, 1.0f)};
+  } else {
+    return float2{exp2_fast(__builtin_fmaf(x, k_in, row)), 1.0f};
   }
 }
 
 template <int CAP>
-__device__ __forceinline__ float capped(float x, float k_in, float c_out) {
-  if constexpr (CAP == kCapFast) return capped_log2_fast(x, k_in, c_out);
-  else if constexpr (CAP == kCapAccurate) return capped_log2_accurate(x, k_in, c_out);
-  else return x * k_in;
+__device__ __forceinline__ float grad_scale(float qs) { return CAP == kCapFast ? 4.0f * qs : qs; }
+
+template <int CAP>
+__device__ __forceinline__ float row_term(float lse, float c_out) {
+  constexpr float kLog2eF = 1.4426950408889634f;
+  return CAP == kCapFast ? c_out - lse * kLog2eF : -lse * kLog2eF;
 }
 
 // ---------------------------------------------------------------- prep
@@ -217,9 +227,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const int tr[2] = {tr_lane_off(l16, lq, 0), tr_lane_off(l16, lq, 1)};
   const float k_in = a.cap.k_in, c_out = a.cap.c_out;
   const float inv_cout = c_out > 0.f ? 1.0f / c_out : 0.f;
-  const float qs = a.query_scale;
-  constexpr float kLog2eF = 1.4426950408889634f;
-
   auto compute = [&](const char (*__restrict__ buf)[TILE], int i) __attribute__((always_inline)) {
     const int hh = i / n_pos;
     const int t0 = t_lo + (i % n_pos) * QT;
@@ -280,11 +287,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = t0 + 16 * qb + 4 * lq + e;
-        const float l2 = lsev[qb][e] * kLog2eF;
-        const float dd = dv4[qb][e];
-        const float s2 = capped<CAP>(sc[qb][e], k_in, c_out);
-        float p = exp2_fast(s2 - l2);
-        float ds = cap_grad<CAP>(p * (dp[qb][e] - dd), s2, inv_cout, qs);
+        const float2 pg = score_terms<CAP>(sc[qb][e], k_in, c_out, inv_cout, row_term<CAP>(lsev[qb][e], c_out));
+        float p = pg.x;
+        float ds = p * (dp[qb][e] - dv4[qb][e]) * pg.y;
         if (need_mask) {
           const int p_ = t + off;
           const bool vis = (t < T) & (j < S) & (j <= p_) & ((j > p_ - win) | !a.is_local);
@@ -341,14 +346,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 
   // dK, dV rows: key jw + l16, dims 16*db + 4*lq .. +3
   const int j = jw + l16;
+  const float gs = grad_scale<CAP>(a.query_scale);
   if (j < S) {
     bf16* kr = a.dk + (((size_t)b * S + j) * KVH + g) * D + 4 * lq;
     bf16* vr = a.dv + (((size_t)b * S + j) * KVH + g) * D + 4 * lq;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       u32x2 wk, wv;
-      wk[0] = pack_bf16x2(dk[db][0], dk[db][1]);
-      wk[1] = pack_bf16x2(dk[db][2], dk[db][3]);
+      wk[0] = pack_bf16x2(dk[db][0] * gs, dk[db][1] * gs);
+      wk[1] = pack_bf16x2(dk[db][2] * gs, dk[db][3] * gs);
       wv[0] = pack_bf16x2(dv[db][0], dv[db][1]);
       wv[1] = pack_bf16x2(dv[db][2], dv[db][3]);
       *reinterpret_cast<u32x2*>(kr + db * 16) = wk;
@@ -403,9 +409,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       of[kk] = __builtin_bit_cast(bf16x8, wo);
     }
   }
-  constexpr float kLog2eF = 1.4426950408889634f;
   const size_t stat = ((size_t)b * H + h) * T + (tq < T ? tq : 0);
-  const float l2 = a.lse[stat] * kLog2eF;
   const float dd = a.dsum[stat];
   f32x4 dq[DB];
 #pragma unroll
@@ -451,7 +455,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int tr[2] = {tr_lane_off(l16, lq, 0), tr_lane_off(l16, lq, 1)};
   const float k_in = a.cap.k_in, c_out = a.cap.c_out;
   const float inv_cout = c_out > 0.f ? 1.0f / c_out : 0.f;
-  const float qs = a.query_scale;
+  const float row = row_term<CAP>(a.lse[stat], c_out);
 
   auto compute = [&](const char (*__restrict__ buf)[TILE], int n0) __attribute__((always_inline)) {
     if (!wave_active || n0 > w_p_last || n0 + BN - 1 < w_j_lo) return;
@@ -477,9 +481,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float s2 = capped<CAP>(st[kb][e], k_in, c_out);
-        const float p = exp2_fast(s2 - l2);
-        float ds = cap_grad<CAP>(p * (dpt[kb][e] - dd), s2, inv_cout, qs);
+        const float2 pg = score_terms<CAP>(st[kb][e], k_in, c_out, inv_cout, row);
+        float ds = pg.x * (dpt[kb][e] - dd) * pg.y;
         if (need_mask) {
           const int j = n0 + 16 * kb + 4 * lq + e;
           const int p_ = tq + off;
@@ -529,11 +532,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
   if (!wave_active || tq >= T) return;
   bf16* qr = a.dq + (((size_t)b * T + tq) * H + h) * D + 4 * lq;
+  const float gs = grad_scale<CAP>(a.query_scale);
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
     u32x2 w2;
-    w2[0] = pack_bf16x2(dq[db][0], dq[db][1]);
-    w2[1] = pack_bf16x2(dq[db][2], dq[db][3]);
+    w2[0] = pack_bf16x2(dq[db][0] * gs, dq[db][1] * gs);
+    w2[1] = pack_bf16x2(dq[db][2] * gs, dq[db][3] * gs);
     *reinterpret_cast<u32x2*>(qr + db * 16) = w2;
   }
 }
