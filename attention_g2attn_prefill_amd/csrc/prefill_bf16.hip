@@ -7,9 +7,10 @@
 // sliding window), softmax over keys, weighted sum of values.
 //
 // Design (MI355X-first):
-//  * One workgroup = 4 waves = 128 query rows that all read the same K/V head:
-//    with two query heads per K/V head (the card's "Method" item 4) that is 64
-//    positions x 2 heads, so every K/V tile staged in LDS serves both heads.
+//  * One workgroup = 8 waves = 256 query rows that all read the same K/V head:
+//    with two query heads per K/V head (the card's "Method" item 4) that is
+//    128 positions x 2 heads, so every K/V tile staged in LDS serves both
+//    heads and eight waves; one workgroup fills a CU (two waves per SIMD).
 //  * K and V tiles go from global memory straight into LDS with
 //    global_load_lds_dwordx4 (no staging registers), double-buffered: the
 //    loads of tile i+1 are in flight while tile i is computed, and one
@@ -53,7 +54,7 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 template <int D, int G, int BN>
 struct PrefillShape {
-  static constexpr int kWaves = 4;
+  static constexpr int kWaves = 8;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kQPW = 32;                 // query rows per wave
   static constexpr int kWPH = kWaves / G;         // waves per query head
@@ -100,7 +101,7 @@ constexpr float kFixedOffsetMaxC = 80.0f;
 constexpr float kFixedOffsetLow = 110.0f;
 
 template <int D, int G, int BN, int CAP, bool FIXED, bool LSE>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(PrefillArgs a) {
   static_assert(!FIXED || CAP == kCapFast, "the constant offset needs the bounded fast cap");
   using P = PrefillShape<D, G, BN>;
   constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
