@@ -327,8 +327,8 @@ def main():
         write_traffic(args.write_traffic[0], args.write_traffic[1], args.calibration_mib)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build "
-              "measures the single-GPU kernels and has no multi-GPU path.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library "
+              "is single-GPU kernels and has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     if args.steps < 1:
         sys.exit("--steps must be >= 1")
