@@ -141,6 +141,32 @@ def test_prefill_rows_saturated_at_the_cap(g2, cap, sign):
         check(synth.to_f32_numpy(out), want, "bf16", f"saturated cap={cap} sign={sign}")
 
 
+@pytest.mark.parametrize("is_local", [True, False], ids=["local", "global"])
+def test_prefill_long_context(g2, is_local):
+    """65536 positions (16x the 9B span), 9B head size and logit scale: sampled
+    rows of the whole prefill and of a 1000-query chunk against the full cache."""
+    B, T, H, KVH, d, W = 1, 65536, 4, 2, 256, 4096
+    say(f"prefill long context T={T} {'local' if is_local else 'global'}")
+    q = synth.draw((B, T, H, d), 51, 0, mul=3.0)
+    k = synth.draw((B, T, KVH, d), 51, 1, mul=3.0)
+    v = synth.draw((B, T, KVH, d), 51, 2)
+    kw = dict(query_scale=1 / 16, softcap=50.0, window=W, is_local=is_local)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    out = g2.prefill(qd, kd, vd, **kw)
+    CT = 1000
+    chunk = g2.prefill(qd[:, T - CT:].contiguous(), kd, vd, **kw)
+    torch.cuda.synchronize()
+    qn, kn, vn = (synth.to_f32_numpy(x) for x in (q, k, v))
+    rng = np.random.default_rng(52)
+    ts = sorted({0, 1, 4095, 4096, 32767, 32768, T - 2, T - 1, *rng.integers(0, T, 24).tolist()})
+    rows = np.asarray([(t * H + h) for t in ts for h in range(H)], np.int64)
+    ref = oracle.prefill(qn, kn, vn, rows=rows, **kw)
+    check(synth.to_f32_numpy(out).reshape(-1, d)[rows], ref, "bf16", f"long context ({rows.size} rows)")
+    crow = np.asarray([(t * H + h) for t in (0, 1, 499, CT - 1) for h in range(H)], np.int64)
+    cref = oracle.prefill(qn[:, T - CT:], kn, vn, rows=crow, **kw)
+    check(synth.to_f32_numpy(chunk).reshape(-1, d)[crow], cref, "bf16", "long-context chunk")
+
+
 # ------------------------------------------------------- full-size prefill
 
 def sample_rows(B, T, H, W, seed, n_random=160):
@@ -358,6 +384,10 @@ DECODE_EDGE = [
     (3, 600, 4, 4, 128, 50, False, "bf16", [600, 1, 333]),
     (3, 300, 4, 2, 256, 64, True, "f32", [5, 300, 999]),
     (2, 300, 4, 2, 64, 64, False, "f32", [300, 7]),
+    # long contexts: a 65536-token linear cache, and a 4096-slot ring that has
+    # wrapped 16 times
+    (2, 65536, 4, 2, 256, 4096, False, "bf16", [65536, 40001]),
+    (2, 4096, 4, 2, 256, 4096, True, "bf16", [65536, 33333]),
 ]
 
 
