@@ -64,7 +64,6 @@ struct PrefillShape {
   static constexpr int kNB = BN / 16;             // 16-key blocks per tile
   static constexpr int kKS = BN / 32;             // 32-key steps of P*V
   static constexpr int kRowBytes = D * 2;
-  static constexpr int kCPR = D / 8;              // 16-byte chunks per row
   static constexpr int kTileBytes = BN * kRowBytes;
   static constexpr int kDmaPerTile = kTileBytes / 1024;   // wave-wide 1 KiB copies
   static constexpr int kDmaPerWave = kDmaPerTile / kWaves;
