@@ -58,6 +58,16 @@ def test_status_strings():
     ((1, 16, 16, 4, 2, 64, 4, 2, 0, 0), ARG),      # is_local not 0/1
     ((1, 16, 16, 4, 2, 96, 4, 0, 0, 0), UNSUP),    # d
     ((1, 16, 16, 8, 2, 64, 4, 0, 0, 0), UNSUP),    # four heads per K/V head
+    ((1, 0, 16, 4, 2, 64, 4, 0, 0, 0), ARG),       # empty query block
+    ((1, 16, 0, 4, 2, 64, 4, 0, 0, 0), ARG),       # empty cache
+    ((1, 16, 16, 0, 2, 64, 4, 0, 0, 0), ARG),      # no heads
+    ((1, 16, 16, 4, 2, 0, 4, 0, 0, 0), ARG),       # d = 0
+    ((1, -5, 16, 4, 2, 64, 4, 0, 0, 0), ARG),      # negative size
+    # element counts per sequence must stay below 2^31 (32-bit in-sequence offsets)
+    ((1, 524287, 524287, 16, 8, 256, 4096, 1, 0, 0), OK),      # T*H*d = 2^31 - 4096
+    ((1, 524288, 524288, 16, 8, 256, 4096, 1, 0, 0), UNSUP),   # T*H*d = 2^31
+    ((1, 1, 1 << 20, 16, 8, 256, 4096, 0, 0, 1), UNSUP),       # S*KVH*d = 2^31 (decode)
+    ((64, 1, (1 << 20) - 1, 16, 8, 256, 4096, 0, 0, 1), OK),   # the longest 9B cache
 ])
 def test_check_args(args, expect):
     assert g2.check_args(*args[:8], dtype=args[8], decode=args[9]) == expect
