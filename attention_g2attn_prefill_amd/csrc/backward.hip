@@ -25,10 +25,11 @@
 //    per wave) and streams 32-key tiles of K and V, like the forward:
 //    S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T.
 // Every tile uses one 16-byte-chunk swizzle, byte (c/4)*R*64 + r*64 +
-// 16*((c%4) ^ sw(r)) for chunk c of row r of an R-row tile, with sw(r) the
-// two bits of (r/4)%4 swapped.  A 64-bank model shows both the row reads
-// (ds_read_b128) and the transpose reads (ds_read_b64_tr_b16) of such a tile
-// free of bank conflicts, so one layout serves both uses of Q, dO and K.
+// 16*((c%4) ^ sw(r)) for chunk c of row r of an R-row tile, with
+// sw(r) = (r/2) % 4.  With it neither the row reads (ds_read_b128) nor the
+// transpose reads (ds_read_b64_tr_b16) of a tile meet a bank conflict (the
+// LDS bank-conflict counter reads zero for both kernels), so one layout
+// serves both uses of Q, dO and K.
 #include "g2_device.h"
 #include "g2_kernels.h"
 
@@ -56,13 +57,14 @@ struct BwdArgs {
   int window, is_local;
 };
 
-__device__ __forceinline__ int swz_rows(int r) { return ((r >> 3) & 1) | (((r >> 2) & 1) << 1); }
+__device__ __forceinline__ int swz_rows(int r) { return (r >> 1) & 3; }
 
 // Transpose-read lane offset inside an R-row tile for column block parity
 // `par`: lane reads row 4*lq + l16/4 at dims 16*db + 4*(l16%4) (rows 16 and
-// 32 further share the swizzle of row 4*lq).
+// 32 further down share that row's swizzle).
 __device__ __forceinline__ int tr_lane_off(int l16, int lq, int par) {
-  return (4 * lq + (l16 >> 2)) * 64 + 16 * (((2 * par) + ((l16 & 3) >> 1)) ^ swz_rows(4 * lq)) + 8 * (l16 & 1);
+  const int r = 4 * lq + (l16 >> 2);
+  return r * 64 + 16 * (((2 * par) + ((l16 & 3) >> 1)) ^ swz_rows(r)) + 8 * (l16 & 1);
 }
 
 // A-operand fragment of rows (tile rows 32*ks + 4*lq + j and + 16) x dims
