@@ -73,10 +73,11 @@ struct PrefillShape {
   static_assert(kDmaPerTile % kWaves == 0, "tile copies split evenly over waves");
 };
 
-// Chunk-in-group swizzles of the K and V tiles (see the layout above).  A
-// ds_read_b128 serves two 8-lane octets per cycle; the K operand read (16 rows,
-// one chunk per 16-lane group) meets no bank conflict with the chunk XORed by
-// (r/2) % 4 (measured with the LDS bank-conflict counter).
+// Chunk-in-group swizzles of the K and V tiles (see the layout above).  With
+// the chunk XORed by (r/2) % 4, the K operand read (16 rows, one chunk per
+// 16-lane group, ds_read_b128) meets no bank conflict, and with the V swizzle
+// neither do the transpose reads (both measured with the LDS bank-conflict
+// counter).
 __device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 3; }
 __device__ __forceinline__ int swz_v(int r) { return ((r >> 2) & 1) << 1; }
 
