@@ -33,6 +33,8 @@
 #include "g2_device.h"
 #include "g2_kernels.h"
 
+#include <type_traits>
+
 namespace g2 {
 
 typedef short s16x4_b __attribute__((ext_vector_type(4)));
@@ -284,24 +286,29 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
         }
     }
     float pv[2][4], dsv[2][4];
+    // the mask test is compiled only into the edge-tile copy of this loop
+    auto scores = [&](auto mask_tag) __attribute__((always_inline)) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = t0 + 16 * qb + 4 * lq + e;
-        const float2 pg = score_terms<CAP>(sc[qb][e], k_in, c_out, inv_cout, row_term<CAP>(lsev[qb][e], c_out));
-        float p = pg.x;
-        float ds = p * (dp[qb][e] - dv4[qb][e]) * pg.y;
-        if (need_mask) {
-          const int p_ = t + off;
-          const bool vis = (t < T) & (j < S) & (j <= p_) & ((j > p_ - win) | !a.is_local);
-          p = vis ? p : 0.f;
-          ds = vis ? ds : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          const float2 pg = score_terms<CAP>(sc[qb][e], k_in, c_out, inv_cout, row_term<CAP>(lsev[qb][e], c_out));
+          float p = pg.x;
+          float ds = p * (dp[qb][e] - dv4[qb][e]) * pg.y;
+          if constexpr (decltype(mask_tag)::value) {
+            const int t = t0 + 16 * qb + 4 * lq + e;
+            const int p_ = t + off;
+            const bool vis = (t < T) & (j < S) & (j <= p_) & ((j > p_ - win) | !a.is_local);
+            p = vis ? p : 0.f;
+            ds = vis ? ds : 0.f;
+          }
+          pv[qb][e] = p;
+          dsv[qb][e] = ds;
         }
-        pv[qb][e] = p;
-        dsv[qb][e] = ds;
       }
-    }
+    };
+    if (need_mask) scores(std::true_type());
+    else scores(std::false_type());
     u32x4 wp, wd;
     wp[0] = pack_bf16x2(pv[0][0], pv[0][1]);
     wp[1] = pack_bf16x2(pv[0][2], pv[0][3]);
@@ -479,21 +486,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       }
     }
     float dsv[2][4];
+    // the mask test is compiled only into the edge-tile copy of this loop
+    auto scores = [&](auto mask_tag) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float2 pg = score_terms<CAP>(st[kb][e], k_in, c_out, inv_cout, row);
-        float ds = pg.x * (dpt[kb][e] - dd) * pg.y;
-        if (need_mask) {
-          const int j = n0 + 16 * kb + 4 * lq + e;
-          const int p_ = tq + off;
-          const bool vis = (tq < T) & (j < S) & (j <= p_) & ((j > p_ - win) | !a.is_local);
-          ds = vis ? ds : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          const float2 pg = score_terms<CAP>(st[kb][e], k_in, c_out, inv_cout, row);
+          float ds = pg.x * (dpt[kb][e] - dd) * pg.y;
+          if constexpr (decltype(mask_tag)::value) {
+            const int j = n0 + 16 * kb + 4 * lq + e;
+            const int p_ = tq + off;
+            const bool vis = (tq < T) & (j < S) & (j <= p_) & ((j > p_ - win) | !a.is_local);
+            ds = vis ? ds : 0.f;
+          }
+          dsv[kb][e] = ds;
         }
-        dsv[kb][e] = ds;
       }
-    }
+    };
+    if (need_mask) scores(std::true_type());
+    else scores(std::false_type());
     u32x4 w;
     w[0] = pack_bf16x2(dsv[0][0], dsv[0][1]);
     w[1] = pack_bf16x2(dsv[0][2], dsv[0][3]);
