@@ -151,6 +151,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int RG = QT / 16;          // 16-row groups per tile
   static_assert(CPW >= 1, "tile copies split evenly over the waves");
   __shared__ __attribute__((aligned(1024))) char lds[2][2][TILE];  // [stage][Q | dO]
+  __shared__ __attribute__((aligned(16))) float stat_lds[2][2 * QT];  // [stage][lse | D] of the tile's rows
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -203,10 +204,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const unsigned q_row_bytes = (unsigned)H * D * 2u;
   const unsigned dma_rl = lane >> 2;
   const unsigned dma_lane = dma_rl * q_row_bytes + (((lane & 3) ^ swz_rows(dma_rl)) * 16u);
-  auto issue = [&](char (*__restrict__ dst)[TILE], int i) __attribute__((always_inline)) {
+  auto issue = [&](char (*__restrict__ dst)[TILE], float* __restrict__ sdst, int i) __attribute__((always_inline)) {
     const int hh = i / n_pos;
     const int t0 = t_lo + (i % n_pos) * QT;
     const int h = g * G + hh;
+    if (wave == 0) {  // the rows' lse (lanes 0..31) and D (lanes 32..63), clamped to row T-1
+      const int tl = t0 + (lane & (QT - 1));
+      const float* src = (lane < QT ? a.lse : a.dsum) + ((size_t)b * H + h) * T + (tl < T ? tl : T - 1);
+      __builtin_amdgcn_global_load_lds(src, G2B_LDS(sdst), 4, 0, 0);
+    }
     const char* qb = reinterpret_cast<const char*>(a.q + ((size_t)b * T * H + h) * D);
     const char* ob = reinterpret_cast<const char*>(a.dout + ((size_t)b * T * H + h) * D);
 #pragma unroll
@@ -231,7 +237,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const int tr[2] = {tr_lane_off(l16, lq, 0), tr_lane_off(l16, lq, 1)};
   const float k_in = a.cap.k_in, c_out = a.cap.c_out;
   const float inv_cout = c_out > 0.f ? 1.0f / c_out : 0.f;
-  auto compute = [&](const char (*__restrict__ buf)[TILE], int i) __attribute__((always_inline)) {
+  auto compute = [&](const char (*__restrict__ buf)[TILE], const float* __restrict__ sbuf, int i) __attribute__((always_inline)) {
     const int hh = i / n_pos;
     const int t0 = t_lo + (i % n_pos) * QT;
     const int h = g * G + hh;
@@ -257,44 +263,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       }
     }
     // P and dS for this lane's key column and its 8 query rows
-    const float* lse_row = a.lse + ((size_t)b * H + h) * T;
-    const float* d_row = a.dsum + ((size_t)b * H + h) * T;
     const int j = jw + l16;
-    // the 8 rows' log-sum-exp and D: 16-byte loads when the tile is whole and
-    // its rows start 16-byte aligned, else one clamped load per row
-    float lsev[2][4], dv4[2][4];
-    if (t0 + QT <= T && (T & 3) == 0) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_row + t0 + 16 * qb + 4 * lq);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(d_row + t0 + 16 * qb + 4 * lq);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lsev[qb][e] = l4[e];
-          dv4[qb][e] = d4[e];
-        }
-      }
-    } else {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = t0 + 16 * qb + 4 * lq + e;
-          const int tc = t < T ? t : T - 1;
-          lsev[qb][e] = lse_row[tc];
-          dv4[qb][e] = d_row[tc];
-        }
-    }
     float pv[2][4], dsv[2][4];
     // the mask test is compiled only into the edge-tile copy of this loop
     auto scores = [&](auto mask_tag) __attribute__((always_inline)) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
+        // the 4 rows' log-sum-exp and D, staged in LDS with the tile
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(sbuf + 16 * qb + 4 * lq);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(sbuf + QT + 16 * qb + 4 * lq);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float2 pg = score_terms<CAP>(sc[qb][e], k_in, c_out, inv_cout, row_term<CAP>(lsev[qb][e], c_out));
+          const float2 pg = score_terms<CAP>(sc[qb][e], k_in, c_out, inv_cout, row_term<CAP>(l4[e], c_out));
           float p = pg.x;
-          float ds = p * (dp[qb][e] - dv4[qb][e]) * pg.y;
+          float ds = p * (dp[qb][e] - d4[e]) * pg.y;
           if constexpr (decltype(mask_tag)::value) {
             const int t = t0 + 16 * qb + 4 * lq + e;
             const int p_ = t + off;
@@ -335,19 +317,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     for (int i = tid; i < (int)(sizeof(lds) / 16); i += 256) z[i] = u32x4{0u, 0u, 0u, 0u};
   }
   __syncthreads();
-  auto step = [&](const char (*__restrict__ cur)[TILE], char (*__restrict__ nxt)[TILE], int i) __attribute__((always_inline)) {
-    if (i + 1 < n_tiles) issue(nxt, i + 1);
-    compute(cur, i);
+  auto step = [&](const char (*__restrict__ cur)[TILE], char (*__restrict__ nxt)[TILE], const float* __restrict__ scur,
+                  float* __restrict__ snxt, int i) __attribute__((always_inline)) {
+    if (i + 1 < n_tiles) issue(nxt, snxt, i + 1);
+    compute(cur, scur, i);
   };
-  issue(lds[0], 0);
+  issue(lds[0], stat_lds[0], 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int i = 0; i < n_tiles; i += 2) {
-    step(lds[0], lds[1], i);
+    step(lds[0], lds[1], stat_lds[0], stat_lds[1], i);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (i + 1 < n_tiles) {
-      step(lds[1], lds[0], i + 1);
+      step(lds[1], lds[0], stat_lds[1], stat_lds[0], i + 1);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
