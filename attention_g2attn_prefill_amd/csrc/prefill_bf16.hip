@@ -221,23 +221,28 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(PrefillArgs a) {
     // ---- S^T = K * Q^T; K operand: row kb*16 + l16, logical chunk 4*kk + lq
     f32x4 st[P::kNB][2];
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    bf16x8 kf[2][P::kNB];  // [parity][kb]: fragments of k-step kk are read one step ahead
+    // fragments of k-step kk are read KD-1 steps ahead (a deeper ring spills
+    // at d = 256, where the scores, Q^T and O^T hold most registers)
+    constexpr int KD = 2;
+    bf16x8 kf[KD][P::kNB];
 #pragma unroll
-    for (int kb = 0; kb < P::kNB; ++kb)
-      kf[0][kb] = *reinterpret_cast<const bf16x8*>(kt + kb * 1024 + k_lane);
+    for (int s0 = 0; s0 < KD - 1; ++s0)
+#pragma unroll
+      for (int kb = 0; kb < P::kNB; ++kb)
+        kf[s0][kb] = *reinterpret_cast<const bf16x8*>(kt + s0 * (BN * 64) + kb * 1024 + k_lane);
 #pragma unroll
     for (int kk = 0; kk < P::kKK; ++kk) {
-      if (kk + 1 < P::kKK) {
+      if (kk + KD - 1 < P::kKK) {
 #pragma unroll
         for (int kb = 0; kb < P::kNB; ++kb)
-          kf[(kk + 1) & 1][kb] = *reinterpret_cast<const bf16x8*>(kt + (kk + 1) * (BN * 64) + kb * 1024 + k_lane);
+          kf[(kk + KD - 1) % KD][kb] = *reinterpret_cast<const bf16x8*>(kt + (kk + KD - 1) * (BN * 64) + kb * 1024 + k_lane);
       }
       __builtin_amdgcn_sched_barrier(0);  // keep the next step's reads ahead of these MFMAs
 #pragma unroll
       for (int kb = 0; kb < P::kNB; ++kb) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          st[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk & 1][kb], qf[qb][kk], kk == 0 ? zero4 : st[kb][qb], 0, 0, 0);
+          st[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk % KD][kb], qf[qb][kk], kk == 0 ? zero4 : st[kb][qb], 0, 0, 0);
       }
     }
 
@@ -368,15 +373,19 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(PrefillArgs a) {
         const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         return __builtin_bit_cast(bf16x8, vv);
       };
-      bf16x8 vf[2];
-      vf[0] = read_v(0);
+      // V fragments are read VD-1 blocks ahead, in the registers the scores
+      // held before they were packed
+      constexpr int VD = 3;
+      bf16x8 vf[VD];
+#pragma unroll
+      for (int s0 = 0; s0 < VD - 1; ++s0) vf[s0] = read_v(s0);
 #pragma unroll
       for (int db = 0; db < P::kDB; ++db) {
-        if (db + 1 < P::kDB) vf[(db + 1) & 1] = read_v(db + 1);
+        if (db + VD - 1 < P::kDB) vf[(db + VD - 1) % VD] = read_v(db + VD - 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db & 1], pf[qb], o[db][qb], 0, 0, 0);
+          o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db % VD], pf[qb], o[db][qb], 0, 0, 0);
       }
     }
   };
