@@ -73,6 +73,10 @@ typedef enum {
  *   is_local    : 1 for a sliding-window (local) layer, 0 for a global layer.
  * Work is proportional to the visible (query, key) pairs: tiles wholly outside
  * the causal / window band are skipped.
+ * Range: for caps up to about 55 the bf16 kernel uses one constant softmax
+ * offset, so an unnormalised weight can reach 2^50; the fp32 accumulators stay
+ * finite while (visible keys of a row) * max|v| < 2^77.  Other caps keep a
+ * running maximum (weights <= 2^8).
  */
 int g2attn_prefill(const void* q, const void* k, const void* v, void* out,
                    int B, int T, int S, int H, int KVH, int d,
