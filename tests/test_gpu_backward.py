@@ -184,3 +184,28 @@ def test_backward_9b_8k_sampled(g2, is_local):
         check_grad(got_q, rq, f"dq rows of group ({b},{g})")
         check_grad(dkn[b, js, g], rk, f"dk keys of group ({b},{g})")
         check_grad(dvn[b, js, g], rv, f"dv keys of group ({b},{g})")
+
+
+def test_backward_lse_at_a_4_byte_offset(g2):
+    """lse need only be 4-byte aligned: a buffer starting one float into an
+    allocation gives the same gradients, bit for bit, as an aligned one."""
+    say("backward with lse at a 4-byte offset")
+    B, T, H, KVH, d = 1, 96, 4, 2, 256
+    q = synth.draw((B, T, H, d), 921, 0, mul=3.0).cuda()
+    k = synth.draw((B, T, KVH, d), 921, 1).cuda()
+    v = synth.draw((B, T, KVH, d), 921, 2).cuda()
+    dout = synth.draw((B, T, H, d), 921, 3).cuda()
+    kw = dict(query_scale=1 / 16, softcap=50.0, window=40, is_local=True)
+    out_a, lse_a = g2.prefill_lse(q, k, v, **kw)
+    base = torch.empty(B * H * T + 1, dtype=torch.float32, device="cuda")
+    lse_b = base[1:].view(B, H, T)
+    assert lse_b.data_ptr() % 16 == 4
+    out_b = torch.empty_like(out_a)
+    g2.prefill_lse(q, k, v, out=out_b, lse=lse_b, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b) and torch.equal(lse_a, lse_b)
+    ga = g2.prefill_backward(q, k, v, out_a, dout, lse_a, **kw)
+    gb = g2.prefill_backward(q, k, v, out_b, dout, lse_b, **kw)
+    torch.cuda.synchronize()
+    for x, y in zip(ga, gb):
+        assert torch.equal(x, y)
