@@ -300,13 +300,17 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const int L = a.kv_lens[b];
   bool ok = decode_len_ok_any<PAGED>(a, L);
   const size_t p0 = (size_t)bh * a.nsplit;
+  // The loops are unrolled so that each issues several splits' loads before
+  // it waits on any of them.
   float mx = kNegInf;
+#pragma unroll 8
   for (int s = 0; s < a.nsplit; ++s) {
     const float ls = a.ws_l[p0 + s];
     if (ls != ls) ok = false;  // a split that could not read its keys
     if (ls > 0.f) mx = fmaxf(mx, a.ws_m[p0 + s]);
   }
   float lsum = 0.f;
+#pragma unroll 8
   for (int s = 0; s < a.nsplit; ++s) {
     const float ls = a.ws_l[p0 + s];
     if (ls > 0.f) lsum += ls * exp2_fast(a.ws_m[p0 + s] - mx);
@@ -315,6 +319,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   E* orow = static_cast<E*>(a.out) + (size_t)bh * D;
   for (int dd = threadIdx.x; dd < D; dd += blockDim.x) {
     float x = 0.f;
+#pragma unroll 8
     for (int s = 0; s < a.nsplit; ++s) {
       const float ls = a.ws_l[p0 + s];
       if (ls > 0.f) x += a.ws_acc[(p0 + s) * D + dd] * exp2_fast(a.ws_m[p0 + s] - mx);
