@@ -152,6 +152,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   static_assert(CPW >= 1, "tile copies split evenly over the waves");
   __shared__ __attribute__((aligned(1024))) char lds[2][2][TILE];  // [stage][Q | dO]
   __shared__ __attribute__((aligned(16))) float stat_lds[2][2 * QT];  // [stage][lse | D] of the tile's rows
+  static_assert(2 * QT == 64, "one wave-wide 4-byte copy stages a tile's lse and D");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
