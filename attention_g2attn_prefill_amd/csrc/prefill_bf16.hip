@@ -44,6 +44,7 @@
 //    XCDs, so each XCD's L2 keeps serving the same K/V heads.
 #include "g2_device.h"
 #include "g2_kernels.h"
+#include <type_traits>
 
 namespace g2 {
 
@@ -221,136 +222,199 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(PrefillArgs a) {
     // ---- S^T = K * Q^T; K operand: row kb*16 + l16, logical chunk 4*kk + lq
     f32x4 st[P::kNB][2];
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    // fragments of k-step kk are read KD-1 steps ahead (a deeper ring spills
-    // at d = 256, where the scores, Q^T and O^T hold most registers)
-    constexpr int KD = 2;
-    bf16x8 kf[KD][P::kNB];
-#pragma unroll
-    for (int s0 = 0; s0 < KD - 1; ++s0)
-#pragma unroll
-      for (int kb = 0; kb < P::kNB; ++kb)
-        kf[s0][kb] = *reinterpret_cast<const bf16x8*>(kt + s0 * (BN * 64) + kb * 1024 + k_lane);
-#pragma unroll
-    for (int kk = 0; kk < P::kKK; ++kk) {
-      if (kk + KD - 1 < P::kKK) {
-#pragma unroll
-        for (int kb = 0; kb < P::kNB; ++kb)
-          kf[(kk + KD - 1) % KD][kb] = *reinterpret_cast<const bf16x8*>(kt + (kk + KD - 1) * (BN * 64) + kb * 1024 + k_lane);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // keep the next step's reads ahead of these MFMAs
-#pragma unroll
-      for (int kb = 0; kb < P::kNB; ++kb) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          st[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk % KD][kb], qf[qb][kk], kk == 0 ? zero4 : st[kb][qb], 0, 0, 0);
-      }
-    }
-
-    // ---- soft-cap + mask.  Fast form keeps r = 1/(1+e^{2y}) (s = C - 2C r,
-    // decreasing in r; masked: r = +inf); other forms keep s (masked: -inf).
-    // The mask test runs only on tiles that cross the band's edges.
-    auto cap_of = [&](float x) __attribute__((always_inline)) {
-      if constexpr (CAP == kCapFast) return rcp_fast(1.0f + exp2_fast(x * k_in));
-      else if constexpr (CAP == kCapAccurate) return capped_log2_accurate(x, k_in, c_out);
-      else return x * k_in;
-    };
-    constexpr float kMasked = (CAP == kCapFast) ? __builtin_inff() : -__builtin_inff();
-    if (need_mask) {
-#pragma unroll
-      for (int kb = 0; kb < P::kNB; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int j = n0 + kb * 16 + lq * 4 + i;
-            const int p = t0 + qb * 16 + l16 + off;
-            const bool vis = (j <= p) & (j < S) & ((j > p - win) | !a.is_local);
-            const float z = cap_of(st[kb][qb][i]);
-            st[kb][qb][i] = vis ? z : kMasked;
-          }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < P::kNB; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) st[kb][qb][i] = cap_of(st[kb][qb][i]);
-    }
-
-    // ---- softmax weights with the constant offset (bounded cap)
-    if constexpr (FIXED) {
+    if constexpr (FIXED && LSE) {
+      // Constant-offset log-sum-exp instance: the scores and weights of the first half of the
+      // key blocks, then those of the second half.  Holding the K fragments of
+      // one half at a time frees the registers the exact row sums need; in
+      // the one-pass order that instance spilled inside the tile loop.
+      constexpr int kH = P::kNB / 2;
       const float base = c_out - a.m_fixed;
       const float slope = -2.0f * c_out;
+      float ls[2] = {0.f, 0.f};
+      auto weight = [&](auto mask_tag, int kb, int qb, int i) __attribute__((always_inline)) {
+        float z = rcp_fast(1.0f + exp2_fast(st[kb][qb][i] * k_in));
+        if constexpr (decltype(mask_tag)::value) {
+          const int j = n0 + kb * 16 + lq * 4 + i;
+          const int p = t0 + qb * 16 + l16 + off;
+          const bool vis = (j <= p) & (j < S) & ((j > p - win) | !a.is_local);
+          z = vis ? z : __builtin_inff();
+        }
+        const float w = exp2_fast(__builtin_fmaf(z, slope, base));
+        st[kb][qb][i] = w;
+        ls[qb] += w;
+      };
+      auto body = [&](auto mask_tag) __attribute__((always_inline)) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float ls = 0.f;
+        for (int half = 0; half < 2; ++half) {
+          const int kb0 = half * kH;
+          bf16x8 kf[2][kH];
 #pragma unroll
-        for (int kb = 0; kb < P::kNB; ++kb)
+          for (int kb = 0; kb < kH; ++kb)
+            kf[0][kb] = *reinterpret_cast<const bf16x8*>(kt + (kb0 + kb) * 1024 + k_lane);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p = exp2_fast(__builtin_fmaf(st[kb][qb][i], slope, base));
-            st[kb][qb][i] = p;
-            if constexpr (LSE) ls += p;
+          for (int kk = 0; kk < P::kKK; ++kk) {
+            if (kk + 1 < P::kKK) {
+#pragma unroll
+              for (int kb = 0; kb < kH; ++kb)
+                kf[(kk + 1) & 1][kb] =
+                    *reinterpret_cast<const bf16x8*>(kt + (kk + 1) * (BN * 64) + (kb0 + kb) * 1024 + k_lane);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kb = 0; kb < kH; ++kb)
+#pragma unroll
+              for (int qb = 0; qb < 2; ++qb)
+                st[kb0 + kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk & 1][kb], qf[qb][kk],
+                                                                           kk == 0 ? zero4 : st[kb0 + kb][qb], 0, 0, 0);
           }
-        if constexpr (LSE) l_run[qb] += ls;
-      }
-    }
-    // ---- online softmax (per lane: two query columns)
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int qb = 0; qb < (FIXED ? 0 : 2); ++qb) {
-      float mt;
-      if constexpr (CAP == kCapFast) {
-        float rmin = __builtin_inff();
+          for (int kb = kb0; kb < kb0 + kH; ++kb)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) weight(mask_tag, kb, qb, i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      if (need_mask) body(std::integral_constant<bool, true>());
+      else body(std::integral_constant<bool, false>());
+      l_run[0] += ls[0];
+      l_run[1] += ls[1];
+    } else {
+      // fragments of k-step kk are read KD-1 steps ahead (a deeper ring spills
+      // at d = 256, where the scores, Q^T and O^T hold most registers)
+      constexpr int KD = 2;
+      bf16x8 kf[KD][P::kNB];
+#pragma unroll
+      for (int s0 = 0; s0 < KD - 1; ++s0)
+#pragma unroll
+        for (int kb = 0; kb < P::kNB; ++kb)
+          kf[s0][kb] = *reinterpret_cast<const bf16x8*>(kt + s0 * (BN * 64) + kb * 1024 + k_lane);
+#pragma unroll
+      for (int kk = 0; kk < P::kKK; ++kk) {
+        if (kk + KD - 1 < P::kKK) {
+#pragma unroll
+          for (int kb = 0; kb < P::kNB; ++kb)
+            kf[(kk + KD - 1) % KD][kb] =
+                *reinterpret_cast<const bf16x8*>(kt + (kk + KD - 1) * (BN * 64) + kb * 1024 + k_lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the next step's reads ahead of these MFMAs
+#pragma unroll
+        for (int kb = 0; kb < P::kNB; ++kb) {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            st[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk % KD][kb], qf[qb][kk],
+                                                                 kk == 0 ? zero4 : st[kb][qb], 0, 0, 0);
+        }
+      }
+
+      // ---- soft-cap + mask.  Fast form keeps r = 1/(1+e^{2y}) (s = C - 2C r,
+      // decreasing in r; masked: r = +inf); other forms keep s (masked: -inf).
+      // The mask test runs only on tiles that cross the band's edges.
+      auto cap_of = [&](float x) __attribute__((always_inline)) {
+        if constexpr (CAP == kCapFast) return rcp_fast(1.0f + exp2_fast(x * k_in));
+        else if constexpr (CAP == kCapAccurate) return capped_log2_accurate(x, k_in, c_out);
+        else return x * k_in;
+      };
+      constexpr float kMasked = (CAP == kCapFast) ? __builtin_inff() : -__builtin_inff();
+      if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < P::kNB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) rmin = fminf(rmin, st[kb][qb][i]);
-        rmin = min_xor16_32_nonneg(rmin);  // r is in [0, 1] or +inf (masked)
-        mt = __builtin_fmaf(-2.0f * c_out, rmin, c_out);  // -inf when all masked
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int j = n0 + kb * 16 + lq * 4 + i;
+              const int p = t0 + qb * 16 + l16 + off;
+              const bool vis = (j <= p) & (j < S) & ((j > p - win) | !a.is_local);
+              const float z = cap_of(st[kb][qb][i]);
+              st[kb][qb][i] = vis ? z : kMasked;
+            }
       } else {
-        mt = kNegInf;
 #pragma unroll
         for (int kb = 0; kb < P::kNB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) mt = fmaxf(mt, st[kb][qb][i]);
-        mt = max_xor16_32(mt);
-      }
-      const bool grow = mt > m_run[qb] + kTau;  // true also for the first visible keys
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float m_new = grow ? mt : m_run[qb];
-        const float alpha = grow ? exp2_fast(m_run[qb] - m_new) : 1.0f;
-        m_run[qb] = m_new;
-        l_run[qb] *= alpha;
-        lsum[qb] *= alpha;
+          for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int db = 0; db < P::kDB; ++db) o[db][qb] *= alpha;
+            for (int i = 0; i < 4; ++i) st[kb][qb][i] = cap_of(st[kb][qb][i]);
       }
-      const float m_use = (m_run[qb] == kNegInf) ? 0.0f : m_run[qb];
-      float ls = 0.f;
-      if constexpr (CAP == kCapFast) {
-        const float base = c_out - m_use;
+
+      // ---- softmax weights with the constant offset (bounded cap)
+      if constexpr (FIXED) {
+        const float base = c_out - a.m_fixed;
         const float slope = -2.0f * c_out;
 #pragma unroll
-        for (int kb = 0; kb < P::kNB; ++kb)
+        for (int qb = 0; qb < 2; ++qb) {
+          float ls = 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p = exp2_fast(__builtin_fmaf(st[kb][qb][i], slope, base));
-            st[kb][qb][i] = p;
-            if constexpr (LSE) ls += p;
-          }
-      } else {
+          for (int kb = 0; kb < P::kNB; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < P::kNB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p = exp2_fast(st[kb][qb][i] - m_use);
-            st[kb][qb][i] = p;
-            if constexpr (LSE) ls += p;
-          }
+            for (int i = 0; i < 4; ++i) {
+              const float p = exp2_fast(__builtin_fmaf(st[kb][qb][i], slope, base));
+              st[kb][qb][i] = p;
+              if constexpr (LSE) ls += p;
+            }
+          if constexpr (LSE) l_run[qb] += ls;
+        }
       }
-      if constexpr (LSE) l_run[qb] += ls;
-    }
+      // ---- online softmax (per lane: two query columns)
+#pragma unroll
+      for (int qb = 0; qb < (FIXED ? 0 : 2); ++qb) {
+        float mt;
+        if constexpr (CAP == kCapFast) {
+          float rmin = __builtin_inff();
+#pragma unroll
+          for (int kb = 0; kb < P::kNB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rmin = fminf(rmin, st[kb][qb][i]);
+          rmin = min_xor16_32_nonneg(rmin);  // r is in [0, 1] or +inf (masked)
+          mt = __builtin_fmaf(-2.0f * c_out, rmin, c_out);  // -inf when all masked
+        } else {
+          mt = kNegInf;
+#pragma unroll
+          for (int kb = 0; kb < P::kNB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mt = fmaxf(mt, st[kb][qb][i]);
+          mt = max_xor16_32(mt);
+        }
+        const bool grow = mt > m_run[qb] + kTau;  // true also for the first visible keys
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+          const float m_new = grow ? mt : m_run[qb];
+          const float alpha = grow ? exp2_fast(m_run[qb] - m_new) : 1.0f;
+          m_run[qb] = m_new;
+          l_run[qb] *= alpha;
+          lsum[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < P::kDB; ++db) o[db][qb] *= alpha;
+        }
+        const float m_use = (m_run[qb] == kNegInf) ? 0.0f : m_run[qb];
+        float ls = 0.f;
+        if constexpr (CAP == kCapFast) {
+          const float base = c_out - m_use;
+          const float slope = -2.0f * c_out;
+#pragma unroll
+          for (int kb = 0; kb < P::kNB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float p = exp2_fast(__builtin_fmaf(st[kb][qb][i], slope, base));
+              st[kb][qb][i] = p;
+              if constexpr (LSE) ls += p;
+            }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < P::kNB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float p = exp2_fast(st[kb][qb][i] - m_use);
+              st[kb][qb][i] = p;
+              if constexpr (LSE) ls += p;
+            }
+        }
+        if constexpr (LSE) l_run[qb] += ls;
+      }
 
+    }  // one-pass order
     // ---- O^T += V^T * P^T; V^T operand rows (keys) 32*ks + 4*lq + j and
     // 32*ks + 16 + 4*lq + j, column (dim) 16*db + l16, via transpose reads
 #pragma unroll
