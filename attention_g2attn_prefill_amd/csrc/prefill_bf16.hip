@@ -124,10 +124,13 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(PrefillArgs a) {
   const int bg = bid % nbg;
   const int b = bg / a.KVH;
   const int g = bg % a.KVH;
-  const int h = g * G + wave / P::kWPH;
+  // Adjacent waves take the G heads of one 32-position block, so the two
+  // waves of a SIMD (w and w + 4) hold different positions and seldom both
+  // skip a tile at the band's edges.
+  const int h = g * G + wave % G;
   const int T = a.T, S = a.S, H = a.H, KVH = a.KVH;
   const int off = S - T;
-  const int t0 = mb * P::kBMP + (wave % P::kWPH) * P::kQPW;  // first row of this wave
+  const int t0 = mb * P::kBMP + (wave / G) * P::kQPW;  // first row of this wave
 
   // ---- Q^T fragments (B operand): lane holds query 16*qb + l16, dims 32*kk + 8*lq .. +7
   bf16x8 qf[2][P::kKK];
