@@ -239,9 +239,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const float k_in = a.cap.k_in, c_out = a.cap.c_out;
   const float inv_cout = c_out > 0.f ? 1.0f / c_out : 0.f;
   auto compute = [&](const char (*__restrict__ buf)[TILE], const float* __restrict__ sbuf, int i) __attribute__((always_inline)) {
-    const int hh = i / n_pos;
     const int t0 = t_lo + (i % n_pos) * QT;
-    const int h = g * G + hh;
     const int p0 = t0 + off;
     const int p_last = min(t0 + QT - 1, T - 1) + off;
     if (jw > p_last || jw >= S) return;

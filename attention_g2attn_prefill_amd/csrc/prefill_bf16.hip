@@ -225,6 +225,20 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(PrefillArgs a) {
     // ---- S^T = K * Q^T; K operand: row kb*16 + l16, logical chunk 4*kk + lq
     f32x4 st[P::kNB][2];
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    // V^T fragment of 32-key step ks and dim block db (two transpose reads)
+    auto read_v = [&](int ks, int db) __attribute__((always_inline)) {
+      const char* vb = vt + (db >> 1) * (BN * 64) + (32 * ks) * 64 + ((db & 1) ? v_lane1 : v_lane0);
+      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G2_LDS_S16X4(vb));
+      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G2_LDS_S16X4(vb + 16 * 64));
+      const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      return __builtin_bit_cast(bf16x8, vv);
+    };
+    // V fragments are read VD-1 blocks ahead.  In the one-pass order the
+    // tile's first one is read before the soft-cap, so the softmax arithmetic
+    // covers its latency (a second one there spills).
+    constexpr int VD = 3;
+    constexpr bool kEarlyV = !(FIXED && LSE);
+    bf16x8 v_early;
     if constexpr (FIXED && LSE) {
       // Constant-offset log-sum-exp instance: the scores and weights of the first half of the
       // key blocks, then those of the second half.  Holding the K fragments of
@@ -312,6 +326,8 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(PrefillArgs a) {
         }
       }
 
+      v_early = read_v(0, 0);
+      __builtin_amdgcn_sched_barrier(0);
       // ---- soft-cap + mask.  Fast form keeps r = 1/(1+e^{2y}) (s = C - 2C r,
       // decreasing in r; masked: r = +inf); other forms keep s (masked: -inf).
       // The mask test runs only on tiles that cross the band's edges.
@@ -433,22 +449,12 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(PrefillArgs a) {
         pf[qb] = __builtin_bit_cast(bf16x8, w);
         lsum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qb], lsum[qb], 0, 0, 0);
       }
-      auto read_v = [&](int db) __attribute__((always_inline)) {
-        const char* vb = vt + (db >> 1) * (BN * 64) + (32 * ks) * 64 + ((db & 1) ? v_lane1 : v_lane0);
-        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G2_LDS_S16X4(vb));
-        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G2_LDS_S16X4(vb + 16 * 64));
-        const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        return __builtin_bit_cast(bf16x8, vv);
-      };
-      // V fragments are read VD-1 blocks ahead, in the registers the scores
-      // held before they were packed
-      constexpr int VD = 3;
       bf16x8 vf[VD];
 #pragma unroll
-      for (int s0 = 0; s0 < VD - 1; ++s0) vf[s0] = read_v(s0);
+      for (int s0 = 0; s0 < VD - 1; ++s0) vf[s0] = (kEarlyV && ks == 0 && s0 == 0) ? v_early : read_v(ks, s0);
 #pragma unroll
       for (int db = 0; db < P::kDB; ++db) {
-        if (db + VD - 1 < P::kDB) vf[(db + VD - 1) % VD] = read_v(db + VD - 1);
+        if (db + VD - 1 < P::kDB) vf[(db + VD - 1) % VD] = read_v(ks, db + VD - 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
