@@ -1,6 +1,8 @@
 """The C ABI from a plain C program (tests/c_abi/c_abi_check.c, built by
-__graft_entry__.build()): prefill and decode on HIP-runtime buffers against the
-CPU oracle, and the documented error statuses, with no Python in the process."""
+__graft_entry__.build()): every compute entry point (prefill, prefill with
+log-sum-exp, backward, decode, paged decode, rotary embedding, final cap) on
+HIP-runtime buffers against the CPU oracle, and the documented error statuses,
+with no Python in the process."""
 import os
 import subprocess
 import sys
