@@ -174,3 +174,22 @@ def test_adjacent_steps_reject_before_launching():
     # nothing to do: no pointer is looked at, nothing is launched
     assert lib.g2attn_softcap(null, 0, 30.0, 0, null) == OK
     assert lib.g2attn_softcap(null, 10, 0.0, 0, null) == OK
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """No fallback: a copy of the package without libg2attn.so raises on first
+    use of an entry point instead of computing anything elsewhere."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = os.path.join(ROOT, "attention_g2attn_prefill_amd")
+    dst = tmp_path / "attention_g2attn_prefill_amd"
+    dst.mkdir()
+    for name in ("__init__.py", "_binding.py", "synth.py"):
+        shutil.copy(os.path.join(pkg, name), dst / name)
+    code = ("import attention_g2attn_prefill_amd as g\n"
+            "try:\n    g.prefill\nexcept ImportError as e:\n    print('raised:', e)\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       cwd=str(tmp_path), timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert "raised:" in r.stdout and "libg2attn.so is not built" in r.stdout
