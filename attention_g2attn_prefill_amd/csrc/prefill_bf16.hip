@@ -236,7 +236,7 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(PrefillArgs a) {
     // V fragments are read VD-1 blocks ahead.  In the one-pass order the
     // tile's first one is read before the soft-cap, so the softmax arithmetic
     // covers its latency (a second one there spills).
-    constexpr int VD = 3;
+    constexpr int VD = 4;
     constexpr bool kEarlyV = !(FIXED && LSE);
     bf16x8 v_early;
     if constexpr (FIXED && LSE) {
