@@ -240,10 +240,11 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(PrefillArgs a) {
     constexpr bool kEarlyV = !(FIXED && LSE);
     bf16x8 v_early;
     if constexpr (FIXED && LSE) {
-      // Constant-offset log-sum-exp instance: the scores and weights of the first half of the
-      // key blocks, then those of the second half.  Holding the K fragments of
-      // one half at a time frees the registers the exact row sums need; in
-      // the one-pass order that instance spilled inside the tile loop.
+      // Constant-offset log-sum-exp instance: the scores and weights of the
+      // first half of the key blocks, then those of the second half.  Holding
+      // the K fragments of one half at a time frees the registers the exact
+      // row sums need; in the one-pass order this instance spilled inside the
+      // tile loop.
       constexpr int kH = P::kNB / 2;
       const float base = c_out - a.m_fixed;
       const float slope = -2.0f * c_out;
