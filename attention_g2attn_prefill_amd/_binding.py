@@ -54,6 +54,8 @@ lib.g2attn_check_args.argtypes = [_I] * 10
 lib.g2attn_check_args.restype = _I
 lib.g2attn_status_string.argtypes = [_I]
 lib.g2attn_status_string.restype = ctypes.c_char_p
+lib.g2attn_build_id.argtypes = []
+lib.g2attn_build_id.restype = ctypes.c_char_p
 
 G2_BF16, G2_F32 = 0, 1
 _DTYPES = {torch.bfloat16: G2_BF16, torch.float32: G2_F32}
@@ -67,6 +69,11 @@ class G2attnError(RuntimeError):
 
 def status_string(status: int) -> str:
     return lib.g2attn_status_string(int(status)).decode()
+
+
+def build_id() -> str:
+    """sha256 of the sources the loaded library was built from."""
+    return lib.g2attn_build_id().decode()
 
 
 def check_args(B, T, S, H, KVH, d, window, is_local, dtype=G2_BF16, decode=False) -> int:
@@ -94,6 +101,17 @@ def _stream_handle(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_workspace(ws, need: int) -> None:
+    """A caller-supplied workspace: a tensor of at least `need` bytes (the
+    library checks the size too; this names the problem before any call)."""
+    if ws is None:
+        return
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError("workspace must be a GPU tensor")
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, needs {need}")
 
 
 def _dev(t: torch.Tensor, name: str):
@@ -174,6 +192,7 @@ def decode(q, k_cache, v_cache, kv_lens, *, query_scale, softcap=50.0, window=40
     if kv_lens.dtype != torch.int32 or tuple(kv_lens.shape) != (B,):
         raise TypeError("kv_lens must be int32 of shape (B,)")
     need = decode_workspace_bytes(B, H, d, S)
+    _check_workspace(workspace, need)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if out is None:
@@ -215,6 +234,8 @@ def decode_paged(q, k_pool, v_pool, block_table, kv_lens, *, query_scale, softca
     if workspace is None:
         need = decode_paged_workspace_bytes(B, H, d, max_blocks, BS)
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    elif not isinstance(workspace, torch.Tensor):
+        raise TypeError("workspace must be a GPU tensor")
     if out is None:
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype:
@@ -275,10 +296,14 @@ def prefill_backward(q, k, v, out, dout, lse, *, query_scale, softcap=50.0, wind
         raise TypeError("the backward pass takes bfloat16 tensors")
     if tuple(lse.shape) != (B, H, T) or lse.dtype != torch.float32:
         raise ValueError("lse must be float32 of shape (B, H, T)")
+    for t, ref, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        if t is not None and (tuple(t.shape) != tuple(ref.shape) or t.dtype != ref.dtype):
+            raise ValueError(f"{name} must have shape {tuple(ref.shape)} and dtype {ref.dtype}")
+    need = int(lib.g2attn_prefill_backward_workspace_bytes(B, T, H))
+    _check_workspace(workspace, need)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    need = int(lib.g2attn_prefill_backward_workspace_bytes(B, T, H))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     st = lib.g2attn_prefill_backward(

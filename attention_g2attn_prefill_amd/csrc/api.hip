@@ -53,7 +53,16 @@ size_t paged_workspace_bytes(int B, int H, int d, int max_blocks, int block_size
 
 }  // namespace
 
+// The sha256 of the sources this library was built from, set by the build
+// script; the tag lets a reader find it in the binary without loading it.
+#ifndef G2ATTN_BUILD_ID
+#define G2ATTN_BUILD_ID "unknown"
+#endif
+static const char kBuildIdRecord[] = "g2attn-build-id:" G2ATTN_BUILD_ID;
+
 extern "C" {
+
+const char* g2attn_build_id(void) { return kBuildIdRecord + sizeof("g2attn-build-id:") - 1; }
 
 int g2attn_check_args(int B, int T, int S, int H, int KVH, int d, int window, int is_local,
                       int dtype, int decode) {

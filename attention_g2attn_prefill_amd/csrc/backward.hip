@@ -32,6 +32,8 @@
 // serves both uses of Q, dO and K.
 #include "g2_device.h"
 #include "g2_kernels.h"
+#define G2_TILES_FN __host__ __device__ inline
+#include "g2_tiles.h"
 
 #include <type_traits>
 
@@ -194,11 +196,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     dv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // query rows that see any of the workgroup's keys: p >= j0 and, on a local
-  // layer, p <= j0 + KB - 1 + win - 1
-  const int t_lo = (max(0, j0 - off) / QT) * QT;
-  const int t_hi = a.is_local ? min(T - 1, j0 + KB - 1 + win - 1 - off) : T - 1;
-  const int n_pos = (t_hi - t_lo) / QT + 1;  // tiles per head
+  // query rows that see any of the workgroup's keys, in QT-row tiles per
+  // head (none: the keys' gradients are zero)
+  const RowTiles rows = rows_seeing_keys(j0, KB, T, S, win, a.is_local, QT);
+  const int t_lo = rows.t_lo;
+  const int n_pos = rows.n_pos;
   const int n_tiles = G * n_pos;
 
   // tile copies (rows t of head h; lanes past T copy nothing)
@@ -240,12 +242,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const float inv_cout = c_out > 0.f ? 1.0f / c_out : 0.f;
   auto compute = [&](const char (*__restrict__ buf)[TILE], const float* __restrict__ sbuf, int i) __attribute__((always_inline)) {
     const int t0 = t_lo + (i % n_pos) * QT;
-    const int p0 = t0 + off;
-    const int p_last = min(t0 + QT - 1, T - 1) + off;
-    if (jw > p_last || jw >= S) return;
-    if (a.is_local && jw + 15 <= p0 - win) return;
-    const bool need_mask = (jw + 15 > p0) || (t0 + QT > T) || (jw + 16 > S) ||
-                           (a.is_local && jw <= p_last - win);
+    const RowBand band = row_band(t0, min(t0 + QT - 1, T - 1), T, S, win, a.is_local);
+    if (jw >= S || keys_unseen(band, jw, 16)) return;
+    const bool need_mask = keys_need_mask(band, jw, 16, S, a.is_local) || (t0 + QT > T);
     const char* qt = buf[0];
     const char* ot = buf[1];
     // S = Q K^T and dP = dO V^T: rows = queries (A from the tile), cols = keys
@@ -321,7 +320,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     if (i + 1 < n_tiles) issue(nxt, snxt, i + 1);
     compute(cur, scur, i);
   };
-  issue(lds[0], stat_lds[0], 0);
+  if (n_tiles > 0) issue(lds[0], stat_lds[0], 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int i = 0; i < n_tiles; i += 2) {
@@ -407,16 +406,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   for (int db = 0; db < DB; ++db) dq[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // keys of the workgroup and of this wave
-  const int wg_p_first = mb * BMP + off;
-  const int wg_p_last = min(mb * BMP + BMP, T) - 1 + off;
-  const int j_lo = a.is_local ? max(0, wg_p_first - win + 1) : 0;
-  const int n_start = (j_lo / BN) * BN;
-  const int n_tiles = (wg_p_last - n_start) / BN + 1;
+  const RowBand wg_band = row_band(mb * BMP, min(mb * BMP + BMP, T) - 1, T, S, win, a.is_local);
+  const KeyTiles wg_tiles = key_tiles(wg_band, BN);
+  const int n_start = wg_tiles.n_start;
+  const int n_tiles = wg_tiles.n_tiles;
   const bool wave_active = t0 < T;
-  const int w_p_first = t0 + off;
-  const int w_p_last = min(t0 + 15, T - 1) + off;
-  const int w_j_lo = a.is_local ? max(0, w_p_first - win + 1) : 0;
-  const int w_j_lo_last = a.is_local ? max(0, w_p_last - win + 1) : 0;
+  const RowBand w_band = row_band(t0, min(t0 + 15, T - 1), T, S, win, a.is_local);
 
   const unsigned kv_row_bytes = (unsigned)KVH * D * 2u;
   const char* kbase = reinterpret_cast<const char*>(a.k + ((size_t)b * S * KVH + g) * D);
@@ -449,9 +444,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const float row = row_term<CAP>(a.lse[stat], c_out);
 
   auto compute = [&](const char (*__restrict__ buf)[TILE], int n0) __attribute__((always_inline)) {
-    if (!wave_active || n0 > w_p_last || n0 + BN - 1 < w_j_lo) return;
-    const bool need_mask = (n0 + BN - 1 > w_p_first) || (n0 + BN > S) ||
-                           (a.is_local && n0 < w_j_lo_last) || (t0 + 16 > T);
+    if (!wave_active || keys_unseen(w_band, n0, BN)) return;
+    const bool need_mask = keys_need_mask(w_band, n0, BN, S, a.is_local) || (t0 + 16 > T);
     const char* kt = buf[0];
     const char* vt = buf[1];
     // S^T = K Q^T and dP^T = V dO^T: rows = keys (A from the tile), cols = queries

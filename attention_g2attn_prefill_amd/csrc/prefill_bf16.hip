@@ -44,6 +44,8 @@
 //    XCDs, so each XCD's L2 keeps serving the same K/V heads.
 #include "g2_device.h"
 #include "g2_kernels.h"
+#define G2_TILES_FN __host__ __device__ inline
+#include "g2_tiles.h"
 #include <type_traits>
 
 namespace g2 {
@@ -147,18 +149,14 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(PrefillArgs a) {
   }
 
   // ---- key range of the workgroup and of this wave
-  const int wg_t_last = min(mb * P::kBMP + P::kBMP, T) - 1;
-  const int wg_p_first = mb * P::kBMP + off;
-  const int wg_p_last = wg_t_last + off;
-  const int j_lo = a.is_local ? max(0, wg_p_first - a.window + 1) : 0;
-  const int n_start = (j_lo / BN) * BN;
-  const int n_tiles = (wg_p_last - n_start) / BN + 1;
+  const RowBand wg_band = row_band(mb * P::kBMP, min(mb * P::kBMP + P::kBMP, T) - 1, T, S,
+                                   a.window, a.is_local);
+  const KeyTiles wg_tiles = key_tiles(wg_band, BN);
+  const int n_start = wg_tiles.n_start;
+  const int n_tiles = wg_tiles.n_tiles;
 
   const bool wave_active = t0 < T;
-  const int w_p_first = t0 + off;
-  const int w_p_last = min(t0 + P::kQPW - 1, T - 1) + off;
-  const int w_j_lo = a.is_local ? max(0, w_p_first - a.window + 1) : 0;
-  const int w_j_lo_last = a.is_local ? max(0, w_p_last - a.window + 1) : 0;
+  const RowBand w_band = row_band(t0, min(t0 + P::kQPW - 1, T - 1), T, S, a.window, a.is_local);
 
   // ---- tile copies.  Copy n fills 16 rows (16*(n % kRowGroups) + lane/4)
   // with chunk group n / kRowGroups; lane i writes physical chunk i%4, which
@@ -216,9 +214,8 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(PrefillArgs a) {
   const int win = a.window;
 
   auto compute_tile = [&](const char (*__restrict__ buf)[P::kTileBytes], int n0) __attribute__((always_inline)) {
-    if (!wave_active || n0 > w_p_last || n0 + BN - 1 < w_j_lo) return;
-    const bool need_mask = (n0 + BN - 1 > w_p_first) || (n0 + BN > S) ||
-                           (a.is_local && n0 < w_j_lo_last);
+    if (!wave_active || keys_unseen(w_band, n0, BN)) return;
+    const bool need_mask = keys_need_mask(w_band, n0, BN, S, a.is_local);
     const char* kt = buf[0];
     const char* vt = buf[1];
 

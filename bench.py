@@ -14,7 +14,11 @@ One step = the whole hot path on seeded synthetic inputs shaped like Gemma 2 9B:
   (30) over the prefill batch's vocabulary logits (2*8192 x 256000, bf16);
   and the backward pass of the 9B local+global pair (dq, dk, dv for a seeded
   upstream gradient), counted as 10*d FLOPs per visible (query head, key) pair
-  (S recomputed, dP, dV, dK, dQ).
+  (S recomputed, dP, dV, dK, dQ); and the local + global prefill pairs of the
+  2B-shaped (B=4, H=8, KVH=4, d=256) and 27B-shaped (B=1, H=32, KVH=16,
+  d=128, query_scale 1/12) workloads.
+  Before each decode launch a 1 GiB buffer is streamed through the caches, so
+  no decode finds its cache rows left in the 256 MB Infinity Cache (MALL).
 
 Reported (one JSON line):
   value    prefill effective TFLOP/s = algorithmic FLOPs of the pair / prefill
@@ -23,7 +27,10 @@ Reported (one JSON line):
   decode   KV GB/s = visible K/V bytes (plus q and out) / decode time;
   roofline the prefill kernel against the bf16 dense MFMA peak (2.5 PFLOP/s),
            durations from HIP events on the launch stream over the timed steps;
-  cpu_baseline the fp64 oracle on a bounded sample of the same workload.
+  cpu_baseline the fp64 oracle on a bounded sample of the same workload, with
+           the host's CPU model, usable CPUs and OMP_NUM_THREADS.
+The library's baked source hash must equal the sources' hash, else the run
+stops: the numbers always describe the code beside this script.
 """
 import argparse
 import glob
@@ -61,16 +68,17 @@ def parse_args():
 
 
 KERNEL_FILES = {  # the sources each measured kernel is built from
-    "prefill": ("prefill_bf16.hip", "g2_device.h", "g2_kernels.h"),
+    "prefill": ("prefill_bf16.hip", "g2_device.h", "g2_kernels.h", "g2_tiles.h"),
     "decode": ("decode.hip", "g2_device.h", "g2_kernels.h"),
 }
 
 
-def kernel_source_hash(which=None):
-    """sha256 of the kernel sources (all of them, or those one kernel is built from)."""
+def kernel_source_hash(which):
+    """sha256 of the sources one measured kernel is built from (the staleness
+    key of the committed counter readings)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "attention_g2attn_prefill_amd", "csrc")
-    names = KERNEL_FILES[which] if which else sorted(os.listdir(csrc))
+    names = KERNEL_FILES[which]
     for name in names:
         with open(os.path.join(csrc, name), "rb") as fh:
             h.update(name.encode())
@@ -169,7 +177,10 @@ def time_adjacent(g2, qd, kd, dev, stream, reps=10, vocab=256000):
     rope_bytes = 2.0 * (q2.numel() + k2.numel()) * q2.element_size()
     cap_bytes = 2.0 * logits.numel() * logits.element_size()
     del q2, k2, logits
-    return {"rope": {"metric": "rotary embedding of Q and K, GB/s", "value": round(rope_bytes / t_rope / 1e9, 1),
+    return {"rope": {"metric": "rotary embedding of Q and K, GB/s",
+                     "parity": "partly unpinned: the pair layout (x[i], x[i+d/2]) and base 10000 "
+                               "are readings, the pages give no rotary formula",
+                     "value": round(rope_bytes / t_rope / 1e9, 1),
                      "frac_of_hbm_peak": round(rope_bytes / t_rope / 1e9 / PEAK_HBM_GBS, 4),
                      "ms": round(t_rope * 1e3, 4), "bytes": rope_bytes},
             "final_softcap": {"metric": "final-logit soft-cap, GB/s",
@@ -294,6 +305,71 @@ def write_traffic(fetch_csv, write_csv, calib_mib):
     print(json.dumps(rec))
 
 
+def host_description():
+    """CPU model, logical CPUs this process may run on, and OMP_NUM_THREADS."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    return {"cpu_model": model, "affinity_cpus": affinity,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+def flush_mall(buf):
+    """Stream a buffer larger than the 256 MB Infinity Cache (MALL) through it,
+    so the next launch finds none of its own data there."""
+    buf.add_(1)
+
+
+def time_models(g2, dev, stream, reps=10):
+    """Prefill local + global layer pairs of the 2B- and 27B-shaped workloads
+    (same kernels as the 9B pair), each layer timed over `reps` launches."""
+    import torch
+    from attention_g2attn_prefill_amd import synth
+    res = {}
+    for name in ("2b-8k", "27b-8k"):
+        cfg = synth.WORKLOADS[name]
+        q, k, v = (x.to(dev) for x in synth.prefill_inputs(cfg))
+        out = torch.empty_like(q)
+        B, T, H, d = q.shape
+        S = k.shape[1]
+        kw = dict(query_scale=cfg["query_scale"], softcap=cfg["softcap"], window=cfg["window"])
+        row = {"shape": {"B": B, "T": T, "S": S, "H": H, "KVH": k.shape[2], "d": d,
+                         "query_scale": cfg["query_scale"], "window": cfg["window"]}}
+        tot_f, tot_t = 0.0, 0.0
+        for is_local in (True, False):
+            g2.prefill(q, k, v, is_local=is_local, out=out, stream=stream, **kw)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                g2.prefill(q, k, v, is_local=is_local, out=out, stream=stream, **kw)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3 / reps
+            f = 4.0 * d * B * H * prefill_pairs(T, S, cfg["window"], is_local)
+            tag = "local" if is_local else "global"
+            row[f"{tag}_ms"] = round(t * 1e3, 4)
+            row[f"{tag}_tflops"] = round(f / t / 1e12, 2)
+            tot_f += f
+            tot_t += t
+        tf = tot_f / tot_t / 1e12
+        row.update({"pair_tflops": round(tf, 2), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                    "flops": tot_f})
+        res[name] = row
+        del q, k, v, out
+    return res
+
+
 def cpu_baseline(cfg, q, k, v, rows_per_layer):
     import numpy as np
     import oracle
@@ -315,7 +391,7 @@ def cpu_baseline(cfg, q, k, v, rows_per_layer):
                        softcap=cfg["softcap"], window=cfg["window"], is_local=is_local)
         secs += time.perf_counter() - t0
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
-            "kind": "oracle",
+            "kind": "oracle", "host": host_description(),
             "sample": (f"{rows_per_layer} seeded random (b,t,h) rows of each layer of the "
                        f"9B 8K local+global pair, every visible key; {secs:.1f} s, "
                        f"{flops / 1e9:.0f} GFLOP counted like the GPU")}
@@ -336,7 +412,14 @@ def main():
     import numpy as np
     import torch
     import attention_g2attn_prefill_amd as g2
+    from attention_g2attn_prefill_amd import build as g2build
     from attention_g2attn_prefill_amd import synth
+
+    # the library must be the one built from the sources beside this script
+    lib_id, src_id = g2.build_id(), g2build.source_hash()
+    if lib_id != src_id:
+        sys.exit(f"{g2.library_path} was built from other sources (id {lib_id}, sources "
+                 f"{src_id}): run __graft_entry__.build() first")
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
@@ -378,6 +461,7 @@ def main():
     pout_g = torch.empty_like(dqd)
     pws = torch.empty(g2.decode_paged_workspace_bytes(DB, DH, Dd, maxb, PBS), dtype=torch.uint8,
                       device=dev)
+    mall = torch.zeros(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB, 4x the MALL
     torch.cuda.synchronize()
 
     kw_p = dict(query_scale=cfg_p["query_scale"], softcap=cfg_p["softcap"], window=W)
@@ -392,18 +476,22 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         g2.prefill(qd, kd, vd, is_local=False, out=out_g, stream=stream, **kw_p)
+        flush_mall(mall)
         if ev is not None:
             ev[2].record(stream)
         g2.decode(dqd, kld, vld, lens_d, is_local=True, out=dout_l, workspace=ws,
                   stream=stream, **kw_d)
+        flush_mall(mall)
         if ev is not None:
             ev[3].record(stream)
         g2.decode(dqd, kgd, vgd, lens_d, is_local=False, out=dout_g, workspace=ws,
                   stream=stream, **kw_d)
+        flush_mall(mall)
         if ev is not None:
             ev[4].record(stream)
         g2.decode_paged(dqd, kpool, vpool, table, lens_d, is_local=True, out=pout_l,
                         workspace=pws, stream=stream, **kw_d)
+        flush_mall(mall)
         if ev is not None:
             ev[5].record(stream)
         g2.decode_paged(dqd, kpool, vpool, table, lens_d, is_local=False, out=pout_g,
@@ -438,6 +526,7 @@ def main():
 
     adjacent = time_adjacent(g2, qd, kd, dev, stream, reps=10)
     backward = time_backward(g2, qd, kd, vd, kw_p, dev, stream, reps=5)
+    models = time_models(g2, dev, stream, reps=10)
     copy_rate = copy_gbs(dev)
     gemm_rate = gemm_tflops(dev)
     if args.copy_calibration_mib > 0:
@@ -468,7 +557,7 @@ def main():
     fc_global = 4.0 * d * B * H * prefill_pairs(CT, S, W, False)
     chunk_tflops = (fc_local + fc_global) / (t_cl + t_cg) / 1e12
 
-    src_hash = kernel_source_hash()
+    src_hash = lib_id  # baked into the loaded library, equal to the sources' hash
     traffic = measured_traffic("prefill", "traffic_bytes_per_launch")
     roofline = {"bound": "mfma", "achieved": round(prefill_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(prefill_tflops / PEAK_BF16_TFLOPS, 4),
@@ -539,6 +628,7 @@ def main():
                           "ms_local": round(t_cl * 1e3, 4), "ms_global": round(t_cg * 1e3, 4),
                           "flops_local": fc_local, "flops_global": fc_global},
         "per_layer": per_layer,
+        "prefill_models": models,
         "kernel_source_sha256": src_hash[:16],
     }
     print(json.dumps(rec), flush=True)

@@ -77,6 +77,12 @@ typedef enum {
  * offset, so an unnormalised weight can reach 2^50; the fp32 accumulators stay
  * finite while (visible keys of a row) * max|v| < 2^77.  Other caps keep a
  * running maximum (weights <= 2^8).
+ * Performance: G2_BF16 is the performance path (MFMA, K/V tiles staged in LDS
+ * and shared by the query heads of a group).  G2_F32 is a correctness path
+ * for small inputs such as a 256-token fp32 layer: one wave per (row, head)
+ * reads every visible K/V row from global memory with plain fp32 arithmetic,
+ * no MFMA and no LDS staging, so its cost grows with T * (visible keys) * H
+ * memory reads; do not use it for long sequences where speed matters.
  */
 int g2attn_prefill(const void* q, const void* k, const void* v, void* out,
                    int B, int T, int S, int H, int KVH, int d,
@@ -228,6 +234,14 @@ int g2attn_check_args(int B, int T, int S, int H, int KVH, int d, int window,
 
 /* Static, human-readable name of a status code. */
 const char* g2attn_status_string(int status);
+
+/*
+ * Static string: the sha256 (64 hex digits) of the sources this library was
+ * built from (its kernel sources, this header and the compiler flags), or
+ * "unknown" for a build that did not set it.  Lets a caller check that the
+ * binary it loaded matches the sources it measures or tests.
+ */
+const char* g2attn_build_id(void);
 
 #ifdef __cplusplus
 }

@@ -48,6 +48,12 @@
 #define G2O_OK 0
 #define G2O_ERR_ARG (-1)
 
+/* sha256 of this source and its compiler flags, set by oracle/build.py. */
+#ifndef G2O_BUILD_ID
+#define G2O_BUILD_ID "unknown"
+#endif
+const char g2o_build_id_record[] = "g2oracle-build-id:" G2O_BUILD_ID;
+
 /* Soft-cap of one logit: cap * tanh(x / cap); the identity when the cap is
  * disabled (cap <= 0 or infinite).  Guide section 1, first formula. */
 double g2o_softcap(double x, double cap) {

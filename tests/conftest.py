@@ -12,15 +12,31 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
 
 
+def _gpu_present() -> bool:
+    # counting devices does not initialise the HIP runtime
+    import torch
+    return torch.cuda.device_count() > 0
+
+
 def _ensure_built():
-    """Build the oracle and the HIP library only if nothing is built yet."""
-    oracle_lib = os.path.join(ROOT, "oracle", "libg2oracle.so")
-    hip_lib = os.path.join(ROOT, "attention_g2attn_prefill_amd", "libg2attn.so")
-    if not os.path.exists(oracle_lib):
-        from oracle import build as ob
+    """The oracle and the HIP library must be built from the sources beside
+    them.  Without a GPU (the build container) a missing or stale library is
+    rebuilt here.  On a GPU machine nothing is compiled: a library whose baked
+    source hash differs from the tree stops the run, so no test ever measures
+    a binary other than the sources it sits next to."""
+    from attention_g2attn_prefill_amd import build as hb
+    from oracle import build as ob
+
+    if not ob.is_current():
+        if _gpu_present() and os.path.exists(ob.LIB):
+            pytest.exit("oracle/libg2oracle.so is stale (built from other sources): run "
+                        "__graft_entry__.build() before the tests", returncode=3)
         ob.build()
-    if not os.path.exists(hip_lib):
-        from attention_g2attn_prefill_amd import build as hb
+    if not hb.is_current():
+        if _gpu_present():
+            pytest.exit(f"{hb.LIB} was built from other sources (id {hb.built_id()}, tree "
+                        f"{hb.source_hash()}): run __graft_entry__.build() before the tests",
+                        returncode=3)
         hb.build()
 
 

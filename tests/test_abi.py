@@ -115,6 +115,44 @@ def test_binding_requires_gpu_tensors():
         g2.prefill(q, k, k, query_scale=0.125, is_local=False)
 
 
+@pytest.mark.parametrize("bad", ["dq", "dk", "dv"])
+def test_backward_rejects_wrong_output_buffers_before_launching(bad):
+    """dq, dk and dv handed in by the caller are checked for shape and dtype
+    before anything reaches the library (the C ABI cannot see their sizes)."""
+    import torch
+    B, T, H, KVH, d = 1, 8, 4, 2, 64
+    q = torch.zeros(B, T, H, d, dtype=torch.bfloat16)
+    k = torch.zeros(B, T, KVH, d, dtype=torch.bfloat16)
+    lse = torch.zeros(B, H, T, dtype=torch.float32)
+    outs = {"dq": torch.zeros_like(q), "dk": torch.zeros_like(k), "dv": torch.zeros_like(k)}
+    short = dict(outs)
+    short[bad] = torch.zeros(outs[bad].numel() - d, dtype=torch.bfloat16).view(-1, d)
+    with pytest.raises(ValueError, match=bad):
+        g2.prefill_backward(q, k, k, q, q, lse, query_scale=0.125, window=4, is_local=True,
+                            **short)
+    wrong_dtype = dict(outs)
+    wrong_dtype[bad] = outs[bad].float()
+    with pytest.raises(ValueError, match=bad):
+        g2.prefill_backward(q, k, k, q, q, lse, query_scale=0.125, window=4, is_local=True,
+                            **wrong_dtype)
+
+
+def test_workspaces_are_checked_before_launching():
+    import torch
+    q = torch.zeros(2, 1, 4, 64, dtype=torch.bfloat16)
+    kc = torch.zeros(2, 16, 2, 64, dtype=torch.bfloat16)
+    lens = torch.ones(2, dtype=torch.int32)
+    need = g2.decode_workspace_bytes(2, 4, 64, 16)
+    with pytest.raises(ValueError, match="workspace"):
+        g2.decode(q, kc, kc, lens, query_scale=0.125, is_local=False,
+                  workspace=torch.zeros(need - 1, dtype=torch.uint8))
+    qb = torch.zeros(1, 8, 4, 64, dtype=torch.bfloat16)
+    kb = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="workspace"):
+        g2.prefill_backward(qb, kb, kb, qb, qb, torch.zeros(1, 4, 8), query_scale=0.125,
+                            window=4, is_local=True, workspace=torch.zeros(3, dtype=torch.uint8))
+
+
 @pytest.mark.parametrize("args,expect", [
     # B, H, KVH, d, block_size, max_blocks, num_blocks, window, is_local, dtype
     ((64, 16, 8, 256, 16, 512, 32768, 4096, 1, 0), OK),

@@ -5,10 +5,12 @@ accumulation, max |diff| <= 2e-2 and mean |diff| <= 2e-3 over the compared
 elements; fp32 storage, max |diff| <= 1e-4.  The oracle consumes exactly the
 values the GPU reads (bf16 values are exact in float32) and returns float64.
 
-Small shapes are compared element by element over the whole output; the
-full-size workloads are compared on sampled rows (first rows, tile and window
-boundaries, the last rows and a seeded random set), with every output also
-checked to be finite.
+Small shapes and the four full-size bf16 workloads (2B, 9B, 9B-sat, 27B, local
+and global layer each) are compared element by element over the whole output;
+decode over all 64 sequences of the 9B workload.  The log-sum-exp and the
+chunked prefill at full size are compared on sampled rows (first rows, tile
+and window boundaries, the last rows and a seeded random set), with every
+output also checked to be finite.
 """
 import sys
 
@@ -184,27 +186,94 @@ def prefill_inputs_cache():
     return {}
 
 
+def _workload_on_gpu(cache, name):
+    """Seeded inputs of a workload on the host (float32 copies for the oracle)
+    and on the GPU; one workload is kept at a time."""
+    if name not in cache:
+        cache.clear()
+        q, k, v = synth.prefill_inputs(synth.WORKLOADS[name])
+        cache[name] = (q, k, v, q.cuda(), k.cuda(), v.cuda(),
+                       synth.to_f32_numpy(k), synth.to_f32_numpy(v))
+    return cache[name]
+
+
+# Whole-output parity of the four full-size bf16 workloads, both layers of
+# each pair: the GPU output is computed once per layer and every element is
+# compared with the oracle, which runs on the host in FULL_CHUNKS contiguous
+# row ranges (flat rows (b*T + t)*H + h) so that each test stays well under a
+# minute on 16 threads.  Each chunk must meet both bounds, so the whole output
+# meets them; the per-layer summary test reports max and mean over all of it.
+FULL_CHUNKS = 4
+FULL_CASES = [(name, is_local, c) for name in ("2b-8k", "9b-8k", "9b-8k-sat", "27b-8k")
+              for is_local in (True, False) for c in range(FULL_CHUNKS)]
+
+
+@pytest.fixture(scope="module")
+def full_outputs():
+    return {"out": {}, "stats": {}}
+
+
+@pytest.mark.parametrize("case", FULL_CASES, ids=[
+    f"{n}-{'local' if l else 'global'}-part{c}" for n, l, c in FULL_CASES])
+def test_prefill_full_size_whole_output(g2, case, prefill_inputs_cache, full_outputs):
+    name, is_local, chunk = case
+    cfg = synth.WORKLOADS[name]
+    layer = "local" if is_local else "global"
+    say(f"prefill full {name} {layer} rows part {chunk + 1}/{FULL_CHUNKS}")
+    q, k, v, qd, kd, vd, kn, vn = _workload_on_gpu(prefill_inputs_cache, name)
+    kw = layer_kw(cfg, is_local)
+    key = (name, is_local)
+    if key not in full_outputs["out"]:
+        full_outputs["out"].clear()
+        out = g2.prefill(qd, kd, vd, **kw)
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(out).all())
+        full_outputs["out"][key] = synth.to_f32_numpy(out)
+    got_all = full_outputs["out"][key]
+    B, T, H, d = q.shape
+    n = B * T * H
+    lo, hi = chunk * n // FULL_CHUNKS, (chunk + 1) * n // FULL_CHUNKS
+    rows = np.arange(lo, hi, dtype=np.int64)
+    ref = oracle.prefill(synth.to_f32_numpy(q), kn, vn, rows=rows, **kw)
+    got = got_all.reshape(-1, d)[lo:hi].astype(np.float64)
+    err = np.abs(got - ref)
+    st = full_outputs["stats"].setdefault(key, {"sum": 0.0, "n": 0, "max": 0.0, "parts": 0})
+    st["sum"] += float(err.sum())
+    st["n"] += err.size
+    st["max"] = max(st["max"], float(err.max()))
+    st["parts"] += 1
+    check(got, ref, cfg["dtype"], f"{name} {layer} rows [{lo}, {hi})")
+
+
 @pytest.mark.parametrize("name", ["2b-8k", "9b-8k", "9b-8k-sat", "27b-8k"])
 @pytest.mark.parametrize("is_local", [True, False], ids=["local", "global"])
-def test_prefill_full_size_sampled(g2, name, is_local, prefill_inputs_cache):
+def test_prefill_full_size_summary(g2, name, is_local, full_outputs):
+    """Max and mean |diff| over every element of the layer's output (all row
+    chunks above), against the stated bounds."""
+    st = full_outputs["stats"].get((name, is_local))
+    if st is None or st["parts"] != FULL_CHUNKS:
+        pytest.skip("run together with test_prefill_full_size_whole_output")
+    mean = st["sum"] / st["n"]
+    say(f"whole output {name} {'local' if is_local else 'global'}: {st['n']} elements, "
+        f"max|d|={st['max']:.3e} mean|d|={mean:.3e}")
+    assert st["max"] <= BF16_MAX and mean <= BF16_MEAN
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny-sat"])
+@pytest.mark.parametrize("is_local", [True, False], ids=["local", "global"])
+def test_tiny_workloads_as_specified(g2, name, is_local):
+    """The fp32 correctness workload exactly as specified (B=1, T=S=256, H=4,
+    KVH=2, d=64, query_scale 1/8, cap 50, window 64, seed 0, q x4; the -sat
+    variant q x32), both layers, every element within 1e-4 of the oracle."""
     cfg = synth.WORKLOADS[name]
-    say(f"prefill full {name} {'local' if is_local else 'global'}")
-    if name not in prefill_inputs_cache:
-        prefill_inputs_cache.clear()
-        q, k, v = synth.prefill_inputs(cfg)
-        prefill_inputs_cache[name] = (q, k, v, q.cuda(), k.cuda(), v.cuda(),
-                                      synth.to_f32_numpy(k), synth.to_f32_numpy(v))
-    q, k, v, qd, kd, vd, kn, vn = prefill_inputs_cache[name]
+    say(f"{name} {'local' if is_local else 'global'}")
+    q, k, v = synth.prefill_inputs(cfg)
+    assert q.dtype == torch.float32
     kw = layer_kw(cfg, is_local)
-    out = g2.prefill(qd, kd, vd, **kw)
+    out = g2.prefill(q.cuda(), k.cuda(), v.cuda(), **kw)
     torch.cuda.synchronize()
-    assert bool(torch.isfinite(out).all())
-    B, T, H, d = q.shape
-    rows = sample_rows(B, T, H, cfg["window"], seed=cfg["seed"])
-    qn = synth.to_f32_numpy(q)
-    ref = oracle.prefill(qn, kn, vn, rows=rows, **kw)
-    got = synth.to_f32_numpy(out).reshape(-1, d)[rows]
-    check(got, ref, cfg["dtype"], f"{name} {'local' if is_local else 'global'} ({rows.size} rows)")
+    ref = oracle.prefill(synth.to_f32_numpy(q), synth.to_f32_numpy(k), synth.to_f32_numpy(v), **kw)
+    check(synth.to_f32_numpy(out), ref, "f32", f"{name} {'local' if is_local else 'global'}")
 
 
 # --------------------------------------------------- log-sum-exp of each row
@@ -247,12 +316,7 @@ def test_prefill_lse_full_size_sampled(g2, is_local, prefill_inputs_cache):
     name = "9b-8k"
     cfg = synth.WORKLOADS[name]
     say(f"prefill lse full {name} {'local' if is_local else 'global'}")
-    if name not in prefill_inputs_cache:
-        prefill_inputs_cache.clear()
-        q, k, v = synth.prefill_inputs(cfg)
-        prefill_inputs_cache[name] = (q, k, v, q.cuda(), k.cuda(), v.cuda(),
-                                      synth.to_f32_numpy(k), synth.to_f32_numpy(v))
-    q, k, v, qd, kd, vd, kn, vn = prefill_inputs_cache[name]
+    q, k, v, qd, kd, vd, kn, vn = _workload_on_gpu(prefill_inputs_cache, name)
     kw = layer_kw(cfg, is_local)
     _, lse = g2.prefill_lse(qd, kd, vd, **kw)
     torch.cuda.synchronize()
@@ -278,12 +342,7 @@ def test_chunked_prefill_9b(g2, T, is_local, prefill_inputs_cache):
     name = "9b-8k"
     cfg = synth.WORKLOADS[name]
     say(f"chunked prefill T={T} {'local' if is_local else 'global'}")
-    if name not in prefill_inputs_cache:
-        prefill_inputs_cache.clear()
-        q, k, v = synth.prefill_inputs(cfg)
-        prefill_inputs_cache[name] = (q, k, v, q.cuda(), k.cuda(), v.cuda(),
-                                      synth.to_f32_numpy(k), synth.to_f32_numpy(v))
-    q, k, v, qd, kd, vd, kn, vn = prefill_inputs_cache[name]
+    q, k, v, qd, kd, vd, kn, vn = _workload_on_gpu(prefill_inputs_cache, name)
     kw = layer_kw(cfg, is_local)
     S = k.shape[1]
     full = g2.prefill(qd, kd, vd, **kw)
@@ -366,13 +425,15 @@ def test_decode_full_size(g2, is_local):
     out = g2.decode(q.cuda(), kc.cuda(), vc.cuda(), torch.from_numpy(lens).cuda(), **kw)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(out).all())
-    # oracle on a sample of sequences (all heads): slices keep the host copy small
-    bs = [0, 1, int(np.argmin(lens)), int(np.argmax(lens)), 17, 40, 63]
-    bs = sorted(set(bs))
-    ref = oracle.decode(synth.to_f32_numpy(q[bs]), synth.to_f32_numpy(kc[bs]),
-                        synth.to_f32_numpy(vc[bs]), lens[bs], **kw)
-    check(synth.to_f32_numpy(out[bs]), ref, "bf16",
-          f"decode {'local' if is_local else 'global'} seqs {bs}")
+    # every sequence, in slices of 8 so the float32 host copies of the caches stay small
+    got = synth.to_f32_numpy(out)
+    refs = []
+    for s0 in range(0, q.shape[0], 8):
+        bs = slice(s0, s0 + 8)
+        refs.append(oracle.decode(synth.to_f32_numpy(q[bs]), synth.to_f32_numpy(kc[bs]),
+                                  synth.to_f32_numpy(vc[bs]), lens[bs], **kw))
+    check(got, np.concatenate(refs), "bf16",
+          f"decode {'local' if is_local else 'global'}, all {q.shape[0]} sequences")
 
 
 DECODE_EDGE = [
