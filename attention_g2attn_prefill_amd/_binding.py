@@ -32,6 +32,9 @@ lib.g2attn_prefill_lse.restype = _I
 lib.g2attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _I, _I, _I, _I, _I, _I, _F, _F, _I,
                               _I, _I, _vp, ctypes.c_size_t, _vp]
 lib.g2attn_decode.restype = _I
+lib.g2attn_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _I, _I, _I, _I, _I, _I, _F, _F,
+                                      _I, _I, _I, _vp]
+lib.g2attn_decode_noalloc.restype = _I
 lib.g2attn_decode_workspace_bytes.argtypes = [_I, _I, _I, _I]
 lib.g2attn_decode_workspace_bytes.restype = ctypes.c_size_t
 lib.g2attn_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _I, _vp, _I, _I, _I, _I, _I, _I,
@@ -206,6 +209,34 @@ def decode(q, k_cache, v_cache, kv_lens, *, query_scale, softcap=50.0, window=40
                            workspace.numel() * workspace.element_size(), _stream_handle(stream))
     if st != 0:
         raise G2attnError(st, "g2attn_decode")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # G2ATTN_NOALLOC_SCRATCH_BYTES
+
+
+def decode_noalloc(q, k_cache, v_cache, kv_lens, *, query_scale, softcap=50.0, window=4096,
+                   is_local, out, stream=None):
+    """decode() through the allocation-free entry point: the split-K scratch is
+    the library's own per-GPU array (at most NOALLOC_SCRATCH_BYTES of
+    workspace), so nothing is allocated; `out` must be given."""
+    B, T, H, d = q.shape
+    Bk, S, KVH, dk = k_cache.shape
+    if (Bk, dk) != (B, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("shape mismatch between q and the caches")
+    if q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and caches must share dtype bfloat16 or float32")
+    if kv_lens.dtype != torch.int32 or tuple(kv_lens.shape) != (B,):
+        raise TypeError("kv_lens must be int32 of shape (B,)")
+    if out is None or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must be given and match q's shape and dtype")
+    st = lib.g2attn_decode_noalloc(_dev(q, "q"), _dev(k_cache, "k_cache"),
+                                   _dev(v_cache, "v_cache"), _dev(out, "out"),
+                                   _dev(kv_lens, "kv_lens"), B, T, S, H, KVH, d,
+                                   float(query_scale), float(softcap), int(window),
+                                   int(bool(is_local)), _DTYPES[q.dtype], _stream_handle(stream))
+    if st != 0:
+        raise G2attnError(st, "g2attn_decode_noalloc")
     return out
 
 

@@ -157,6 +157,28 @@ int g2attn_decode(const void* q, const void* k_cache, const void* v_cache,
 size_t g2attn_decode_workspace_bytes(int B, int H, int d, int S);
 
 /*
+ * Allocation-free decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, behaviour and results as g2attn_decode, but
+ * without the workspace: the split-K scratch is a device array of
+ * G2ATTN_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, held
+ * until the process ends.  The call allocates nothing.
+ *   Limit: g2attn_decode_workspace_bytes(B, H, d, S) must not exceed
+ *   G2ATTN_NOALLOC_SCRATCH_BYTES (32 MiB: the 9B-shaped decode at S = 8192
+ *   fits up to B = 127), else G2_ERR_WORKSPACE is returned before any launch.
+ *   All calls on one GPU share its scratch array: calls that overlap in time
+ *   on one GPU (different streams, or different host threads) race and must
+ *   be serialised by the caller.  The first call on a device looks up the
+ *   array's device address (a host-side query, no allocation).
+ */
+#define G2ATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+int g2attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                          void* out, const int32_t* kv_lens,
+                          int B, int T, int S, int H, int KVH, int d,
+                          float query_scale, float softcap, int window, int is_local,
+                          int dtype, hipStream_t stream);
+
+/*
  * Decode against a paged KV cache (Gemma 2 Guide, "Deep Dive" item 2: serving
  * runtimes keep KV memory in fixed-size blocks, and local layers drop the
  * blocks older than the window).
