@@ -247,17 +247,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     const bool need_mask = keys_need_mask(band, jw, 16, S, a.is_local) || (t0 + QT > T);
     const char* qt = buf[0];
     const char* ot = buf[1];
-    // S = Q K^T and dP = dO V^T: rows = queries (A from the tile), cols = keys
+    // S = Q K^T and dP = dO V^T: rows = queries (A from the tile), cols = keys;
+    // the tile fragments of k-step kk + 1 are read before the MFMAs of kk
     f32x4 sc[2], dp[2];
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
+    bf16x8 qa[2][2], oa[2][2];  // [stage][16-row block]
+    auto load_a = [&](int sg, int kk) __attribute__((always_inline)) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qt + kk * (QT * 64) + qb * 1024 + k_lane);
-        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(ot + kk * (QT * 64) + qb * 1024 + k_lane);
-        sc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kfr[kk], kk == 0 ? zero4 : sc[qb], 0, 0, 0);
-        dp[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, vfr[kk], kk == 0 ? zero4 : dp[qb], 0, 0, 0);
+        qa[sg][qb] = *reinterpret_cast<const bf16x8*>(qt + kk * (QT * 64) + qb * 1024 + k_lane);
+        oa[sg][qb] = *reinterpret_cast<const bf16x8*>(ot + kk * (QT * 64) + qb * 1024 + k_lane);
+      }
+    };
+    load_a(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      if (kk + 1 < KK) load_a((kk + 1) & 1, kk + 1);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        sc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk & 1][qb], kfr[kk], kk == 0 ? zero4 : sc[qb], 0, 0, 0);
+        dp[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa[kk & 1][qb], vfr[kk], kk == 0 ? zero4 : dp[qb], 0, 0, 0);
       }
     }
     // P and dS for this lane's key column and its 8 query rows
@@ -448,17 +457,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     const bool need_mask = keys_need_mask(w_band, n0, BN, S, a.is_local) || (t0 + 16 > T);
     const char* kt = buf[0];
     const char* vt = buf[1];
-    // S^T = K Q^T and dP^T = V dO^T: rows = keys (A from the tile), cols = queries
+    // S^T = K Q^T and dP^T = V dO^T: rows = keys (A from the tile), cols =
+    // queries; the tile fragments of k-step kk + 1 are read before the MFMAs of kk
     f32x4 st[2], dpt[2];
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
+    bf16x8 ka[2][2], va[2][2];  // [stage][16-key block]
+    auto load_a = [&](int sg, int kk) __attribute__((always_inline)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + kk * (BN * 64) + kb * 1024 + k_lane);
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vt + kk * (BN * 64) + kb * 1024 + k_lane);
-        st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[kk], kk == 0 ? zero4 : st[kb], 0, 0, 0);
-        dpt[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, of[kk], kk == 0 ? zero4 : dpt[kb], 0, 0, 0);
+        ka[sg][kb] = *reinterpret_cast<const bf16x8*>(kt + kk * (BN * 64) + kb * 1024 + k_lane);
+        va[sg][kb] = *reinterpret_cast<const bf16x8*>(vt + kk * (BN * 64) + kb * 1024 + k_lane);
+      }
+    };
+    load_a(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      if (kk + 1 < KK) load_a((kk + 1) & 1, kk + 1);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk & 1][kb], qf[kk], kk == 0 ? zero4 : st[kb], 0, 0, 0);
+        dpt[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[kk & 1][kb], of[kk], kk == 0 ? zero4 : dpt[kb], 0, 0, 0);
       }
     }
     float dsv[2][4];
