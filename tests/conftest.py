@@ -43,6 +43,16 @@ def _ensure_built():
 _ensure_built()
 
 
+def pytest_terminal_summary(terminalreporter):
+    """Print the GPU tests' measurements (max / mean differences against the
+    oracle, bounds) even though pytest captured them."""
+    import _report
+    if _report.LINES:
+        terminalreporter.section("parity measurements")
+        for line in _report.LINES:
+            terminalreporter.write_line(line)
+
+
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")

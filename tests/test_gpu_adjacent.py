@@ -14,6 +14,7 @@ import torch
 
 import oracle
 from attention_g2attn_prefill_amd import synth
+from _report import report
 
 pytestmark = pytest.mark.gpu
 
@@ -43,7 +44,7 @@ def check_storage(got, ref, dtype, what, f32_tol=2e-5, arith=None):
     got = np.asarray(got, np.float64)
     assert np.all(np.isfinite(got)), what
     err = np.abs(got - ref)
-    say(f"{what}: max|d|={err.max():.3e}")
+    report(f"{what}: max|d|={err.max():.3e}")
     if dtype == "f32":
         assert err.max() <= f32_tol, what
     else:

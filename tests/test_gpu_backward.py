@@ -27,6 +27,7 @@ import torch
 
 import oracle
 from attention_g2attn_prefill_amd import synth
+from _report import report
 
 pytestmark = pytest.mark.gpu
 
@@ -56,7 +57,7 @@ def check_grad(got, ref, what):
         pe = err.mean(axis=(0, 2, 3)) / np.maximum(np.abs(ref).mean(axis=(0, 2, 3)), 1e-30)
         worst = np.argsort(pe)[-5:][::-1]
         say(f"{what}: worst positions {[(int(t), round(float(pe[t]), 4)) for t in worst]}")
-    say(f"{what}: max|d|/max|ref|={err.max() / max(scale_max, 1e-30):.3e} "
+    report(f"{what}: max|d|/max|ref|={err.max() / max(scale_max, 1e-30):.3e} "
         f"mean|d|/mean|ref|={err.mean() / max(scale_mean, 1e-30):.3e}")
     assert scale_max > 0, f"{what}: all-zero reference (use the self-only test)"
     assert err.max() <= REL_MAX * scale_max, what
@@ -150,7 +151,7 @@ def test_backward_rows_that_see_only_themselves(g2, case):
     bq = (1 + 2.0 ** -7) * qs * np.abs(np.repeat(kn, G, axis=2)) * R[..., None]
     bk = (1 + 2.0 ** -7) * qs * (np.abs(qn) * R[..., None]).reshape(B, T, KVH, G, d).sum(axis=3)
     gq, gk = synth.to_f32_numpy(dq).astype(np.float64), synth.to_f32_numpy(dk).astype(np.float64)
-    say(f"self-only {case}: max|dq|={np.abs(gq).max():.3e} (bound {bq.max():.3e}), "
+    report(f"self-only {case}: max|dq|={np.abs(gq).max():.3e} (bound {bq.max():.3e}), "
         f"max|dk|={np.abs(gk).max():.3e} (bound {bk.max():.3e}), "
         f"max ratio dq {np.max(np.abs(gq) / bq):.3f} dk {np.max(np.abs(gk) / bk):.3f}")
     assert np.all(np.abs(gq) <= bq) and np.all(np.abs(gk) <= bk)
@@ -236,7 +237,7 @@ def test_backward_9b_8k_sampled(g2, is_local):
     bound = 5 * 2.0 ** -9 * np.sqrt((g64 ** 2).sum(axis=(1, 3)))
     got = dvn.sum(axis=1)
     err = np.abs(got - want)
-    say(f"sum dv over keys: max|d|={err.max():.3e}, max |d|/bound={np.max(err / bound):.3f}")
+    report(f"sum dv over keys: max|d|={err.max():.3e}, max |d|/bound={np.max(err / bound):.3f}")
     assert np.all(err <= bound)
 
     rng = np.random.default_rng(41)

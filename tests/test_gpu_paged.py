@@ -16,6 +16,7 @@ import torch
 
 import oracle
 from attention_g2attn_prefill_amd import synth
+from _report import report
 
 pytestmark = pytest.mark.gpu
 
@@ -41,7 +42,7 @@ def check(got, ref, dtype, what):
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     err = np.abs(got - ref)
     mx, mean = float(err.max()), float(err.mean())
-    say(f"{what}: max|d|={mx:.3e} mean|d|={mean:.3e}")
+    report(f"{what}: max|d|={mx:.3e} mean|d|={mean:.3e}")
     if dtype == "f32":
         assert mx <= F32_MAX, f"{what}: max {mx}"
     else:

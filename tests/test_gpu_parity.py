@@ -20,6 +20,7 @@ import torch
 
 import oracle
 from attention_g2attn_prefill_amd import synth
+from _report import report
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +46,7 @@ def check(got, ref, dtype, what):
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     err = np.abs(got - ref)
     mx, mean = float(err.max()), float(err.mean())
-    say(f"{what}: max|d|={mx:.3e} mean|d|={mean:.3e}")
+    report(f"{what}: max|d|={mx:.3e} mean|d|={mean:.3e}")
     if dtype == "f32":
         assert mx <= F32_MAX, f"{what}: max {mx}"
     else:
@@ -254,7 +255,7 @@ def test_prefill_full_size_summary(g2, name, is_local, full_outputs):
     if st is None or st["parts"] != FULL_CHUNKS:
         pytest.skip("run together with test_prefill_full_size_whole_output")
     mean = st["sum"] / st["n"]
-    say(f"whole output {name} {'local' if is_local else 'global'}: {st['n']} elements, "
+    report(f"whole output {name} {'local' if is_local else 'global'}: {st['n']} elements, "
         f"max|d|={st['max']:.3e} mean|d|={mean:.3e}")
     assert st["max"] <= BF16_MAX and mean <= BF16_MEAN
 
@@ -307,7 +308,7 @@ def test_prefill_lse(g2, case):
     qn, kn = synth.to_f32_numpy(q), synth.to_f32_numpy(k)
     ref = oracle.prefill_lse(qn, kn, **kw).transpose(0, 2, 1)     # (B, H, T)
     err = np.abs(lse.cpu().numpy().astype(np.float64) - ref)
-    say(f"lse {case}: max|d|={err.max():.3e}")
+    report(f"lse {case}: max|d|={err.max():.3e}")
     assert np.all(np.isfinite(err)) and err.max() <= (LSE_F32_MAX if dt == "f32" else LSE_BF16_MAX)
 
 
@@ -326,7 +327,7 @@ def test_prefill_lse_full_size_sampled(g2, is_local, prefill_inputs_cache):
     b, t, h = rows // (T * H), (rows // H) % T, rows % H
     got = lse.cpu().numpy()[b, h, t].astype(np.float64)
     err = np.abs(got - ref)
-    say(f"lse full: max|d|={err.max():.3e} over {rows.size} rows")
+    report(f"lse full: max|d|={err.max():.3e} over {rows.size} rows")
     assert np.all(np.isfinite(got)) and err.max() <= LSE_BF16_MAX
 
 

@@ -11,6 +11,7 @@ import torch
 
 import oracle
 from attention_g2attn_prefill_amd import synth
+from _report import report
 
 pytestmark = pytest.mark.gpu
 
@@ -69,7 +70,7 @@ def test_noalloc_decode_equals_decode_on_two_calls(g2):
         want = oracle.decode(synth.to_f32_numpy(q[:nb]), synth.to_f32_numpy(kc[:nb]),
                              synth.to_f32_numpy(vc[:nb]), lens[:nb], **kw)
         err = np.abs(synth.to_f32_numpy(out[:nb]).astype(np.float64) - want)
-        say(f"call {i + 1}: equal to g2attn_decode; vs oracle max|d|={err.max():.3e} "
+        report(f"call {i + 1}: equal to g2attn_decode; vs oracle max|d|={err.max():.3e} "
             f"mean|d|={err.mean():.3e}")
         assert err.max() <= 2e-2 and err.mean() <= 2e-3
 
