@@ -47,7 +47,7 @@ lib.g2attn_check_paged_args.restype = _I
 lib.g2attn_prefill_backward.argtypes = [_vp] * 9 + [_I] * 6 + [_F, _F, _I, _I, _I, _vp,
                                                                 ctypes.c_size_t, _vp]
 lib.g2attn_prefill_backward.restype = _I
-lib.g2attn_prefill_backward_workspace_bytes.argtypes = [_I, _I, _I]
+lib.g2attn_prefill_backward_workspace_bytes.argtypes = [_I, _I, _I, _I]
 lib.g2attn_prefill_backward_workspace_bytes.restype = ctypes.c_size_t
 lib.g2attn_rope.argtypes = [_vp, _vp, _I, _I, _I, _I, _F, _I, _vp]
 lib.g2attn_rope.restype = _I
@@ -311,6 +311,15 @@ def softcap_(x, cap=30.0, stream=None):
     return x
 
 
+def backward_workspace_bytes(B, T, S, H):
+    """Bytes of workspace prefill_backward needs (row statistics and the bf16
+    dS blocks, about 2*B*T*S*H bytes)."""
+    n = int(lib.g2attn_prefill_backward_workspace_bytes(int(B), int(T), int(S), int(H)))
+    if n == 0:
+        raise ValueError(f"invalid backward sizes B={B} T={T} S={S} H={H}")
+    return n
+
+
 def prefill_backward(q, k, v, out, dout, lse, *, query_scale, softcap=50.0, window=4096,
                      is_local, dq=None, dk=None, dv=None, workspace=None, stream=None):
     """Gradients (dq, dk, dv) of the prefill for an upstream gradient dout of
@@ -330,7 +339,7 @@ def prefill_backward(q, k, v, out, dout, lse, *, query_scale, softcap=50.0, wind
     for t, ref, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
         if t is not None and (tuple(t.shape) != tuple(ref.shape) or t.dtype != ref.dtype):
             raise ValueError(f"{name} must have shape {tuple(ref.shape)} and dtype {ref.dtype}")
-    need = int(lib.g2attn_prefill_backward_workspace_bytes(B, T, H))
+    need = backward_workspace_bytes(B, T, S, H)
     _check_workspace(workspace, need)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk

@@ -187,9 +187,9 @@ int g2attn_softcap(void* x, size_t n, float cap, int dtype, hipStream_t stream) 
   return g2::launch_softcap(x, n, cap, dtype, stream) == hipSuccess ? G2_OK : G2_ERR_LAUNCH;
 }
 
-size_t g2attn_prefill_backward_workspace_bytes(int B, int T, int H) {
-  if (B <= 0 || T <= 0 || H <= 0) return 0;
-  return (size_t)B * H * T * sizeof(float);
+size_t g2attn_prefill_backward_workspace_bytes(int B, int T, int S, int H) {
+  if (B <= 0 || T <= 0 || S < T || H <= 0) return 0;
+  return g2::backward_workspace_bytes(B, T, S, H);
 }
 
 int g2attn_prefill_backward(const void* q, const void* k, const void* v, const void* out,
@@ -205,8 +205,8 @@ int g2attn_prefill_backward(const void* q, const void* k, const void* v, const v
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return G2_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return G2_ERR_ALIGN;
-  if (!workspace || workspace_bytes < (size_t)B * H * T * sizeof(float)) return G2_ERR_WORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0) return G2_ERR_ALIGN;
+  if (!workspace || workspace_bytes < g2::backward_workspace_bytes(B, T, S, H)) return G2_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return G2_ERR_ALIGN;
   g2::BackwardLaunch L{q, k, v, out, dout, lse, dq, dk, dv, B, T, S, H, KVH, d,
                        query_scale, softcap, window, is_local, workspace};
   return g2::launch_prefill_backward(L, stream) == hipSuccess ? G2_OK : G2_ERR_LAUNCH;

@@ -20,16 +20,21 @@
 //    the stationary fragments as B; each lane then holds one key column and
 //    eight query rows, so P and dS are formed in registers and feed
 //    dV^T += dO^T P and dK^T += Q^T dS with the tile's transpose (the LDS
-//    transpose read) as A operand;
-//  * dQ, query-stationary: a workgroup owns 32 positions of both heads (16 rows
-//    per wave) and streams 32-key tiles of K and V, like the forward:
-//    S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T.
+//    transpose read) as A operand.  The bf16 dS of the tile (the operand of
+//    dK) is also stored to the workspace, 1 KiB per wave, as 16 key rows of
+//    32 query columns;
+//  * dQ, query-stationary: dQ = dS K needs no recomputation of S and dP.  A
+//    workgroup owns BMP positions of the heads of one K/V head and streams
+//    32-key tiles of K and the matching stored dS blocks through
+//    double-buffered LDS; a wave holds dQ^T for 64 rows of one head and up to
+//    128 dims and forms dQ^T += K^T dS^T with both operands from transpose
+//    reads.
 // Every tile uses one 16-byte-chunk swizzle, byte (c/4)*R*64 + r*64 +
 // 16*((c%4) ^ sw(r)) for chunk c of row r of an R-row tile, with
 // sw(r) = (r/2) % 4.  With it neither the row reads (ds_read_b128) nor the
-// transpose reads (ds_read_b64_tr_b16) of a tile meet a bank conflict (the
-// LDS bank-conflict counter reads zero for both kernels), so one layout
-// serves both uses of Q, dO and K.
+// transpose reads (ds_read_b64_tr_b16) of a tile meet a bank conflict, so
+// one layout serves both uses of Q, dO, K and dS.  The stored dS blocks are
+// not swizzled; the dQ kernel's copies apply the swizzle.
 #include "g2_device.h"
 #include "g2_kernels.h"
 #define G2_TILES_FN __host__ __device__ inline
@@ -52,6 +57,9 @@ struct BwdArgs {
   const bf16* dout;
   const float* lse;  // (B, H, T), natural log
   float* dsum;       // (B, H, T): D = <dO, out>, written by the prep kernel
+  char* ds;          // dS blocks, 1 KiB per (b, h, 32-row tile, 16-key block)
+  int n_tt, n_kb;    // 32-row tiles and 16-key blocks per (b, h)
+  float dq_scale;    // dQ = dq_scale * dS K
   bf16* dq;
   bf16* dk;
   bf16* dv;
@@ -104,7 +112,7 @@ __device__ __forceinline__ float2 score_terms(float x, float k_in, float c_out, 
 }
 
 template <int CAP>
-__device__ __forceinline__ float grad_scale(float qs) { return CAP == kCapFast ? 4.0f * qs : qs; }
+__host__ __device__ inline float grad_scale(float qs) { return CAP == kCapFast ? 4.0f * qs : qs; }
 
 template <int CAP>
 __device__ __forceinline__ float row_term(float lse, float c_out) {
@@ -155,6 +163,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[2][2][TILE];  // [stage][Q | dO]
   __shared__ __attribute__((aligned(16))) float stat_lds[2][2 * QT];  // [stage][lse | D] of the tile's rows
   static_assert(2 * QT == 64, "one wave-wide 4-byte copy stages a tile's lse and D");
+  static_assert(QT == kDsRows && KB / 4 == kDsKeys, "a wave's tile is one stored dS block");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -309,6 +318,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     wd[3] = pack_bf16x2(dsv[1][2], dsv[1][3]);
     const bf16x8 pb = __builtin_bit_cast(bf16x8, wp);
     const bf16x8 sb = __builtin_bit_cast(bf16x8, wd);
+    {  // dS^T of the block for the dQ kernel: key row l16, query columns 4*lq.. and 16 + 4*lq..
+       // Non-temporal (the dQ kernel reads it, this kernel never does), and
+       // issued here rather than sunk to the tile's end, a tile's dK/dV
+       // MFMAs ahead of the wait that ends the tile.
+      const int h = g * G + i / n_pos;
+      char* blk = a.ds + ((((size_t)b * H + h) * a.n_tt + t0 / kDsRows) * a.n_kb + jw / kDsKeys) * 1024;
+      __builtin_nontemporal_store(u32x2{wd[0], wd[1]}, reinterpret_cast<u32x2*>(blk + l16 * 64 + 8 * lq));
+      __builtin_nontemporal_store(u32x2{wd[2], wd[3]}, reinterpret_cast<u32x2*>(blk + l16 * 64 + 32 + 8 * lq));
+      asm volatile("" ::: "memory");
+    }
     // dV^T += dO^T P, dK^T += Q^T dS (k = the tile's 32 query rows)
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -363,18 +382,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- dQ
-template <int D, int G, int CAP>
+template <int D, int G>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int BN = 32;               // keys per tile
-  constexpr int KK = D / 32;
-  constexpr int DB = D / 16;
-  constexpr int TILE = BN * D * 2;
-  constexpr int CPW = TILE / 1024 / 4;
-  constexpr int RG = BN / 16;
-  constexpr int WPH = 4 / G;           // waves per query head
-  constexpr int BMP = 16 * WPH;        // positions per workgroup
-  static_assert(CPW >= 1, "tile copies split evenly over the waves");
-  __shared__ __attribute__((aligned(1024))) char lds[2][2][TILE];  // [stage][K | V]
+  constexpr int BN = 32;                 // keys per tile
+  constexpr int DW = D < 128 ? D : 128;  // dims per wave
+  constexpr int ND = D / DW;             // waves per (head, 64 rows)
+  constexpr int NQ = 4 / (G * ND);       // 64-row blocks per head
+  constexpr int BMP = 64 * NQ;           // positions per workgroup
+  constexpr int DBW = DW / 16;           // 16-dim blocks per wave
+  constexpr int KTILE = BN * D * 2;      // bytes of a K tile
+  constexpr int TPH = BMP / kDsRows;     // dS row tiles per head
+  constexpr int DSB = G * TPH * 2;       // 1 KiB dS blocks per key tile
+  constexpr int NK = KTILE / 1024;       // 1 KiB copies of K per key tile
+  constexpr int NC = (NK + DSB) / 4;     // 1 KiB copies per wave and key tile
+  static_assert(G * ND * NQ == 4 && NK % 4 == 0 && DSB % 4 == 0, "copies split evenly over the waves");
+  static_assert(BN == 2 * kDsKeys, "a key tile holds two dS key blocks");
+  __shared__ __attribute__((aligned(1024))) char lds[2][KTILE + DSB * 1024];  // [stage][K | dS blocks]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -382,176 +405,136 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int l16 = lane & 15;
   const int lq = lane >> 4;
   const int T = a.T, S = a.S, H = a.H, KVH = a.KVH;
+  const int win = a.window, is_local = a.is_local;
   const int nbg = a.B * KVH;
   const int n_mb = (T + BMP - 1) / BMP;
   const int mb = n_mb - 1 - (int)(blockIdx.x / nbg);  // heaviest first
   const int bg = blockIdx.x % nbg;
   const int b = bg / KVH, g = bg % KVH;
-  const int h = g * G + wave / WPH;
-  const int t0 = mb * BMP + (wave % WPH) * 16;  // this wave's first row
-  const int off = S - T;
-  const int win = a.window;
+  const int hh = wave / (ND * NQ);     // head of the K/V head's group
+  const int qi = (wave / ND) % NQ;     // 64-row block of the workgroup
+  const int dp = wave % ND;            // dims [DW * dp, DW * dp + DW)
+  const int h = g * G + hh;
+  const int m0 = mb * BMP;
+  const int tw = m0 + 64 * qi;         // this wave's first row
+  const int tt0 = m0 / kDsRows;        // the workgroup's first dS row tile
 
-  // stationary B operands: Q^T and dO^T of query t0 + l16, dims 32*kk + 8*lq
-  const int tq = t0 + l16;
-  bf16x8 qf[KK], of[KK];
-  {
-    const size_t r = ((size_t)b * T + (tq < T ? tq : 0)) * H + h;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      u32x4 wq = {0u, 0u, 0u, 0u}, wo = {0u, 0u, 0u, 0u};
-      if (tq < T) {
-        wq = *reinterpret_cast<const u32x4*>(a.q + r * D + kk * 32 + lq * 8);
-        wo = *reinterpret_cast<const u32x4*>(a.dout + r * D + kk * 32 + lq * 8);
-      }
-      qf[kk] = __builtin_bit_cast(bf16x8, wq);
-      of[kk] = __builtin_bit_cast(bf16x8, wo);
-    }
-  }
-  const size_t stat = ((size_t)b * H + h) * T + (tq < T ? tq : 0);
-  const float dd = a.dsum[stat];
-  f32x4 dq[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) dq[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // keys of the workgroup and of this wave
-  const RowBand wg_band = row_band(mb * BMP, min(mb * BMP + BMP, T) - 1, T, S, win, a.is_local);
+  const RowBand wg_band = row_band(m0, min(m0 + BMP, T) - 1, T, S, win, is_local);
   const KeyTiles wg_tiles = key_tiles(wg_band, BN);
   const int n_start = wg_tiles.n_start;
   const int n_tiles = wg_tiles.n_tiles;
-  const bool wave_active = t0 < T;
-  const RowBand w_band = row_band(t0, min(t0 + 15, T - 1), T, S, win, a.is_local);
+  const bool wave_active = tw < T;
+  const RowBand w_band = row_band(tw, min(tw + 63, T - 1), T, S, win, is_local);
 
+  // copies: K rows past S and dS blocks no row sees are not copied (the
+  // fragments of such blocks are zeroed in compute)
   const unsigned kv_row_bytes = (unsigned)KVH * D * 2u;
   const char* kbase = reinterpret_cast<const char*>(a.k + ((size_t)b * S * KVH + g) * D);
-  const char* vbase = reinterpret_cast<const char*>(a.v + ((size_t)b * S * KVH + g) * D);
+  const size_t head_blocks = (size_t)a.n_tt * a.n_kb;
+  const char* dsbase = a.ds + ((size_t)b * H + (size_t)g * G) * head_blocks * 1024;
   const unsigned dma_rl = lane >> 2;
-  const unsigned dma_lane = dma_rl * kv_row_bytes + (((lane & 3) ^ swz_rows(dma_rl)) * 16u);
-  auto issue = [&](char (*__restrict__ dst)[TILE], int n0) __attribute__((always_inline)) {
+  const unsigned k_src = dma_rl * kv_row_bytes + (((lane & 3) ^ swz_rows(dma_rl)) * 16u);
+  const unsigned ds_src = dma_rl * 64u + (((lane & 3) ^ swz_rows(dma_rl)) * 16u);
+  auto issue = [&](char* __restrict__ dst, int n0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-      const int n = wave + c * 4;
-      const int cg = n / RG, r0 = 16 * (n % RG);
-      const size_t uni = (size_t)(n0 + r0) * kv_row_bytes + 64u * cg;
-      const char* rk = kbase + uni;
-      const char* rv = vbase + uni;
-      unsigned lo = dma_lane;
-      asm volatile("" : "+s"(rk));
-      asm volatile("" : "+s"(rv));
-      asm volatile("" : "+v"(lo));
-      if (n0 + r0 + (int)dma_rl < S) {
-        __builtin_amdgcn_global_load_lds(rk + lo, G2B_LDS(&dst[0][n * 1024]), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(rv + lo, G2B_LDS(&dst[1][n * 1024]), 16, 0, 0);
+    for (int c = 0; c < NC; ++c) {
+      const int n = wave + 4 * c;
+      if (4 * c < NK) {  // K rows n0 + 16 * (n % 2) .., dims 32 * (n / 2) ..
+        const int r0 = 16 * (n & 1);
+        const char* rk = kbase + (size_t)(n0 + r0) * kv_row_bytes + 64u * (n >> 1);
+        unsigned lo = k_src;
+        asm volatile("" : "+s"(rk));
+        asm volatile("" : "+v"(lo));
+        if (n0 + r0 + (int)dma_rl < S)
+          __builtin_amdgcn_global_load_lds(rk + lo, G2B_LDS(dst + n * 1024), 16, 0, 0);
+      } else {  // dS block (head hx, row tile tt0 + tl, key block n0/16 + kl)
+        const int m = n - NK;
+        const int hx = m / (2 * TPH), tl = (m >> 1) % TPH, kl = m & 1;
+        const int tt = tt0 + tl, kb = n0 / kDsKeys + kl;
+        if (ds_block_seen(tt, kb, T, S, win, is_local)) {
+          const char* rd = dsbase + (((size_t)hx * a.n_tt + tt) * a.n_kb + kb) * 1024;
+          unsigned lo = ds_src;
+          asm volatile("" : "+s"(rd));
+          asm volatile("" : "+v"(lo));
+          __builtin_amdgcn_global_load_lds(rd + lo, G2B_LDS(dst + n * 1024), 16, 0, 0);
+        }
       }
     }
   };
 
-  const int k_lane = l16 * 64 + ((lq ^ swz_rows(l16)) << 4);
   const int tr[2] = {tr_lane_off(l16, lq, 0), tr_lane_off(l16, lq, 1)};
-  const float k_in = a.cap.k_in, c_out = a.cap.c_out;
-  const float inv_cout = c_out > 0.f ? 1.0f / c_out : 0.f;
-  const float row = row_term<CAP>(a.lse[stat], c_out);
+  f32x4 acc[DBW][4];
+#pragma unroll
+  for (int i = 0; i < DBW; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[i][r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const char (*__restrict__ buf)[TILE], int n0) __attribute__((always_inline)) {
+  auto compute = [&](const char* __restrict__ buf, int n0) __attribute__((always_inline)) {
     if (!wave_active || keys_unseen(w_band, n0, BN)) return;
-    const bool need_mask = keys_need_mask(w_band, n0, BN, S, a.is_local) || (t0 + 16 > T);
-    const char* kt = buf[0];
-    const char* vt = buf[1];
-    // S^T = K Q^T and dP^T = V dO^T: rows = keys (A from the tile), cols =
-    // queries; the tile fragments of k-step kk + 1 are read before the MFMAs of kk
-    f32x4 st[2], dpt[2];
-    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    bf16x8 ka[2][2], va[2][2];  // [stage][16-key block]
-    auto load_a = [&](int sg, int kk) __attribute__((always_inline)) {
+    // B = dS^T of the wave's 16-row blocks r: rows = the tile's keys; the
+    // halves of a fragment (keys 4*lq.. and 16 + 4*lq..) come from the two
+    // key blocks and are zero where no row of the block's row tile sees them
+    const char* dst = buf + KTILE + (hh * TPH + 2 * qi) * 2048;
+    bf16x8 bq[4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        ka[sg][kb] = *reinterpret_cast<const bf16x8*>(kt + kk * (BN * 64) + kb * 1024 + k_lane);
-        va[sg][kb] = *reinterpret_cast<const bf16x8*>(vt + kk * (BN * 64) + kb * 1024 + k_lane);
-      }
-    };
-    load_a(0, 0);
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if (kk + 1 < KK) load_a((kk + 1) & 1, kk + 1);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk & 1][kb], qf[kk], kk == 0 ? zero4 : st[kb], 0, 0, 0);
-        dpt[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[kk & 1][kb], of[kk], kk == 0 ? zero4 : dpt[kb], 0, 0, 0);
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int tt = tt0 + 2 * qi + (r >> 1);
+      u32x4 w = __builtin_bit_cast(u32x4, read_tr<32>(dst + (r >> 1) * 2048, r & 1, 0, tr));
+      if (!ds_block_seen(tt, n0 / kDsKeys, T, S, win, is_local)) w[0] = w[1] = 0u;
+      if (!ds_block_seen(tt, n0 / kDsKeys + 1, T, S, win, is_local)) w[2] = w[3] = 0u;
+      bq[r] = __builtin_bit_cast(bf16x8, w);
     }
-    float dsv[2][4];
-    // the mask test is compiled only into the edge-tile copy of this loop
-    auto scores = [&](auto mask_tag) __attribute__((always_inline)) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float2 pg = score_terms<CAP>(st[kb][e], k_in, c_out, inv_cout, row);
-          float ds = pg.x * (dpt[kb][e] - dd) * pg.y;
-          if constexpr (decltype(mask_tag)::value) {
-            const int j = n0 + 16 * kb + 4 * lq + e;
-            const int p_ = tq + off;
-            const bool vis = (tq < T) & (j < S) & (j <= p_) & ((j > p_ - win) | !a.is_local);
-            ds = vis ? ds : 0.f;
-          }
-          dsv[kb][e] = ds;
-        }
-      }
-    };
-    if (need_mask) scores(std::true_type());
-    else scores(std::false_type());
-    u32x4 w;
-    w[0] = pack_bf16x2(dsv[0][0], dsv[0][1]);
-    w[1] = pack_bf16x2(dsv[0][2], dsv[0][3]);
-    w[2] = pack_bf16x2(dsv[1][0], dsv[1][1]);
-    w[3] = pack_bf16x2(dsv[1][2], dsv[1][3]);
-    const bf16x8 sb = __builtin_bit_cast(bf16x8, w);
     // dQ^T += K^T dS^T (k = the tile's 32 keys)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const bf16x8 kT = read_tr<BN>(kt, db, 0, tr);
-      dq[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kT, sb, dq[db], 0, 0, 0);
+    for (int i = 0; i < DBW; ++i) {
+      const bf16x8 kT = read_tr<BN>(buf, dp * DBW + i, 0, tr);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kT, bq[r], acc[i][r], 0, 0, 0);
     }
   };
 
   {
-    u32x4* z = reinterpret_cast<u32x4*>(&lds[0][0][0]);
+    u32x4* z = reinterpret_cast<u32x4*>(&lds[0][0]);
     for (int i = tid; i < (int)(sizeof(lds) / 16); i += 256) z[i] = u32x4{0u, 0u, 0u, 0u};
   }
   __syncthreads();
-  auto step = [&](const char (*__restrict__ cur)[TILE], char (*__restrict__ nxt)[TILE], int n0, bool more) __attribute__((always_inline)) {
-    if (more) issue(nxt, n0 + BN);
-    compute(cur, n0);
-  };
   issue(lds[0], n_start);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int it = 0; it < n_tiles; it += 2) {
     const int n0 = n_start + it * BN;
-    step(lds[0], lds[1], n0, it + 1 < n_tiles);
+    if (it + 1 < n_tiles) issue(lds[1], n0 + BN);
+    compute(lds[0], n0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (it + 1 < n_tiles) {
-      step(lds[1], lds[0], n0 + BN, it + 2 < n_tiles);
+      if (it + 2 < n_tiles) issue(lds[0], n0 + 2 * BN);
+      compute(lds[1], n0 + BN);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
   }
 
-  if (!wave_active || tq >= T) return;
-  bf16* qr = a.dq + (((size_t)b * T + tq) * H + h) * D + 4 * lq;
-  const float gs = grad_scale<CAP>(a.query_scale);
+  if (!wave_active) return;
+  const float gs = a.dq_scale;
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    u32x2 w2;
-    w2[0] = pack_bf16x2(dq[db][0] * gs, dq[db][1] * gs);
-    w2[1] = pack_bf16x2(dq[db][2] * gs, dq[db][3] * gs);
-    *reinterpret_cast<u32x2*>(qr + db * 16) = w2;
+  for (int r = 0; r < 4; ++r) {
+    const int t = tw + 16 * r + l16;
+    if (t >= T) continue;
+    bf16* qr = a.dq + (((size_t)b * T + t) * H + h) * D + DW * dp + 4 * lq;
+#pragma unroll
+    for (int i = 0; i < DBW; ++i) {
+      u32x2 w2;
+      w2[0] = pack_bf16x2(acc[i][r][0] * gs, acc[i][r][1] * gs);
+      w2[1] = pack_bf16x2(acc[i][r][2] * gs, acc[i][r][3] * gs);
+      *reinterpret_cast<u32x2*>(qr + i * 16) = w2;
+    }
   }
 }
 
 template <int D, int G, int CAP>
-static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+static hipError_t launch_bwd_t(BwdArgs a, hipStream_t stream) {
+  a.dq_scale = grad_scale<CAP>(a.query_scale);
   const long rows = (long)a.B * a.T * a.H;
   const unsigned gp = (unsigned)((rows * (D / 8) + 255) / 256);
   hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3(gp), dim3(256), 0, stream, a);
@@ -562,9 +545,10 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, G, CAP>), dim3(gk), dim3(256), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int BMP = 16 * (4 / G);
+  constexpr int ND = D > 128 ? D / 128 : 1;
+  constexpr int BMP = 64 * (4 / (G * ND));  // the dQ kernel's positions per workgroup
   const unsigned gq = (unsigned)((a.T + BMP - 1) / BMP) * nbg;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, G, CAP>), dim3(gq), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, G>), dim3(gq), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -586,6 +570,9 @@ hipError_t launch_prefill_backward(const BackwardLaunch& L, hipStream_t stream) 
   a.dout = static_cast<const bf16*>(L.dout);
   a.lse = L.lse;
   a.dsum = static_cast<float*>(L.workspace);
+  a.ds = static_cast<char*>(L.workspace) + backward_ds_offset(L.B, L.T, L.H);
+  a.n_tt = (L.T + kDsRows - 1) / kDsRows;
+  a.n_kb = (L.S + kDsKeys - 1) / kDsKeys;
   a.dq = static_cast<bf16*>(L.dq);
   a.dk = static_cast<bf16*>(L.dk);
   a.dv = static_cast<bf16*>(L.dv);

@@ -67,8 +67,22 @@ struct BackwardLaunch {
   int B, T, S, H, KVH, d;
   float query_scale, softcap;
   int window, is_local;
-  void* workspace;   // (B, H, T) fp32
+  void* workspace;   // backward_workspace_bytes(B, T, S, H) bytes, layout below
 };
+
+// Backward workspace: D = <dO, out> per row, float (B, H, T), then, from a
+// 256-byte boundary, the dS blocks: for each (b, h, 32-row tile, 16-key
+// block) 1 KiB holding dS^T of the block as 16 key rows of 32 bf16 (one per
+// query row), in that order.
+inline size_t backward_ds_offset(int B, int T, int H) {
+  return ((size_t)B * H * T * sizeof(float) + 255) & ~(size_t)255;
+}
+inline size_t backward_ds_blocks(int B, int T, int S, int H) {
+  return (size_t)B * H * (size_t)((T + 31) / 32) * (size_t)((S + 15) / 16);
+}
+inline size_t backward_workspace_bytes(int B, int T, int S, int H) {
+  return backward_ds_offset(B, T, H) + backward_ds_blocks(B, T, S, H) * 1024;
+}
 
 hipError_t launch_prefill_backward(const BackwardLaunch& L, hipStream_t stream);
 

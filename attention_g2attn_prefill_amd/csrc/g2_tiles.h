@@ -100,4 +100,18 @@ G2_TILES_FN RowTiles rows_seeing_keys(int j0, int KB, int T, int S, int W, int i
   return r;
 }
 
+// The backward's dS blocks: dS for query rows [32 tt, 32 tt + 32) of one head
+// and keys [16 kb, 16 kb + 16).  The key-stationary kernel writes exactly the
+// blocks for which this is true (every other block is all zero and is never
+// written); the dQ kernel reads exactly those.  Blocks past T or S are unseen.
+constexpr int kDsRows = 32;
+constexpr int kDsKeys = 16;
+
+G2_TILES_FN bool ds_block_seen(int tt, int kb, int T, int S, int W, int is_local) {
+  const int t_first = tt * kDsRows, j0 = kb * kDsKeys;
+  if (tt < 0 || kb < 0 || t_first >= T || j0 >= S) return false;
+  const RowBand r = row_band(t_first, tiles_imin(t_first + kDsRows - 1, T - 1), T, S, W, is_local);
+  return !keys_unseen(r, j0, kDsKeys);
+}
+
 }  // namespace g2

@@ -223,7 +223,7 @@ def time_backward(g2, qd, kd, vd, kw, dev, stream, reps=5):
     for is_local in (True, False):
         out, lse = g2.prefill_lse(qd, kd, vd, is_local=is_local, stream=stream, **kw)
         dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
-        ws = torch.empty(B * H * T * 4, dtype=torch.uint8, device=dev)
+        ws = torch.empty(g2.backward_workspace_bytes(B, T, S, H), dtype=torch.uint8, device=dev)
         warm(lambda: g2.prefill_backward(qd, kd, vd, out, dout, lse, is_local=is_local, dq=dq,
                                          dk=dk, dv=dv, workspace=ws, stream=stream, **kw))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

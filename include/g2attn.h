@@ -111,8 +111,12 @@ int g2attn_prefill_lse(const void* q, const void* k, const void* v, void* out,
  *   over every row that sees a key.
  * q, k, v and the scalars are those of the forward call; out and lse are its
  * results (g2attn_prefill_lse).  bf16 only (fp32: G2_ERR_UNSUPPORTED).
- * workspace: device scratch of g2attn_prefill_backward_workspace_bytes(B,T,H)
- * bytes (one float per row).  Buffers may not alias each other.
+ * workspace: device scratch of g2attn_prefill_backward_workspace_bytes(B,T,S,H)
+ * bytes, 16-byte aligned: one float per row and, for each (batch, head,
+ * 32-row tile, 16-key block), 1 KiB of bf16 dS = p (<dO, v> - D) (1 - tanh^2)
+ * that the dK/dV kernel stores and the dQ kernel reads, about 2 B T S H bytes
+ * in all (4.3 GB for B = 2, T = S = 8192, H = 16).  Buffers may not alias
+ * each other.  G2_ERR_WORKSPACE if the workspace is missing or too small.
  */
 int g2attn_prefill_backward(const void* q, const void* k, const void* v,
                             const void* out, const void* dout, const float* lse,
@@ -123,7 +127,7 @@ int g2attn_prefill_backward(const void* q, const void* k, const void* v,
                             hipStream_t stream);
 
 /* Bytes of backward workspace for these sizes (0 for invalid sizes). */
-size_t g2attn_prefill_backward_workspace_bytes(int B, int T, int H);
+size_t g2attn_prefill_backward_workspace_bytes(int B, int T, int S, int H);
 
 /*
  * Decode: one new query token per sequence against a KV cache of capacity S

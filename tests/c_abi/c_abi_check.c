@@ -245,7 +245,7 @@ int main(void) {
     HIP_OK(hipMalloc(&gdq, nq * 2));
     HIP_OK(hipMalloc(&gdk, nk * 2));
     HIP_OK(hipMalloc(&gdv, nk * 2));
-    const size_t bwsb = g2attn_prefill_backward_workspace_bytes(B, T, H);
+    const size_t bwsb = g2attn_prefill_backward_workspace_bytes(B, T, S, H);
     HIP_OK(hipMalloc(&bws, bwsb));
     st = g2attn_prefill_backward(dq, dk2, dv, dout, dgo, dlse, gdq, gdk, gdv, B, T, S, H, KVH, d, qs,
                                  cap, W, 1, G2_BF16, bws, bwsb, stream);

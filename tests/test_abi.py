@@ -73,6 +73,16 @@ def test_check_args(args, expect):
     assert g2.check_args(*args[:8], dtype=args[8], decode=args[9]) == expect
 
 
+def test_backward_workspace_bytes():
+    # row statistics (rounded up to 256 bytes), then 1 KiB per (b, h, 32-row tile, 16-key block)
+    assert g2.backward_workspace_bytes(2, 8192, 8192, 16) == 2 * 16 * 8192 * 4 + 2 * 16 * 256 * 512 * 1024
+    assert g2.backward_workspace_bytes(1, 1, 1, 1) == 256 + 1024
+    assert g2.backward_workspace_bytes(1, 33, 40, 3) == 512 + 3 * 2 * 3 * 1024
+    for bad in ((0, 4, 4, 1), (1, 5, 4, 1), (1, 4, 4, 0)):
+        with pytest.raises(ValueError):
+            g2.backward_workspace_bytes(*bad)
+
+
 def test_workspace_bytes():
     # splits of 512 positions; per (sequence, head, split): max, sum, d floats
     assert g2.decode_workspace_bytes(64, 16, 256, 8192) == 64 * 16 * 16 * (2 + 256) * 4

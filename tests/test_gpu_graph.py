@@ -60,7 +60,7 @@ def test_step_in_a_hip_graph_replays_bit_exact(g2):
             loc=torch.empty_like(q), glo=torch.empty_like(q), lout=torch.empty_like(q),
             lse=torch.empty((B, H, T), dtype=torch.float32, device=dev),
             dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
-            bws=torch.empty(g2.lib.g2attn_prefill_backward_workspace_bytes(B, T, H),
+            bws=torch.empty(g2.backward_workspace_bytes(B, T, T, H),
                             dtype=torch.uint8, device=dev),
             dring=torch.empty_like(dq_), dlin=torch.empty_like(dq_), dpag=torch.empty_like(dq_),
             ws1=torch.empty(g2.decode_workspace_bytes(DB, H, d, RS), dtype=torch.uint8, device=dev),

@@ -8,7 +8,10 @@
 // For each (T, S, W, local) of a grid, and each kernel's blocking:
 //   * every visible pair lies in a tile the kernel walks and does not skip;
 //   * every tile walked without the mask holds only visible pairs;
-//   * walked key tiles start inside [0, S); row tiles start inside [0, T).
+//   * walked key tiles start inside [0, S); row tiles start inside [0, T);
+//   * the backward's dS blocks (32 rows x 16 keys) that the key-stationary
+//     kernel writes are exactly those holding a visible pair, and it visits
+//     every one of them.
 // Prints one line per failure and "tile check: N cases, 0 failures" at the end;
 // the exit status is the number of failures (capped at 100).
 #include <climits>
@@ -93,6 +96,30 @@ static void check_key_blocked(int T, int S, int W, int local, int KB, int KW, in
   }
 }
 
+// dS blocks: seen iff the block holds a visible pair; the dK/dV kernel
+// (blocks of KB keys, waves of 16 keys, row tiles of 32) reaches every seen one.
+static void check_ds_blocks(int T, int S, int W, int local, int KB) {
+  const int n_tt = (T + kDsRows - 1) / kDsRows + 1, n_kb = (S + kDsKeys - 1) / kDsKeys + 1;
+  for (int tt = 0; tt < n_tt; ++tt)
+    for (int kb = 0; kb < n_kb; ++kb) {
+      bool any = false;
+      for (int t = tt * kDsRows; t < (tt + 1) * kDsRows && t < T && !any; ++t)
+        for (int j = kb * kDsKeys; j < (kb + 1) * kDsKeys && j < S && !any; ++j) any = visible(t, j, T, S, W, local);
+      const bool seen = ds_block_seen(tt, kb, T, S, W, local);
+      if (seen != any) fail(any ? "dS block with a visible pair not seen" : "dS block seen without a visible pair", T, S, W, local, tt, kb);
+      if (!seen) continue;
+      const int j0 = (kb * kDsKeys / KB) * KB, jw = kb * kDsKeys;
+      const RowTiles rt = rows_seeing_keys(j0, KB, T, S, W, local, kDsRows);
+      if (tt * kDsRows < rt.t_lo || tt * kDsRows >= rt.t_lo + rt.n_pos * kDsRows) {
+        fail("seen dS block outside the dK/dV kernel's rows", T, S, W, local, tt, kb);
+        continue;
+      }
+      const int t0 = tt * kDsRows, t1 = (t0 + kDsRows - 1 < T - 1 ? t0 + kDsRows - 1 : T - 1);
+      if (jw >= S || keys_unseen(row_band(t0, t1, T, S, W, local), jw, kDsKeys))
+        fail("seen dS block skipped by the dK/dV kernel", T, S, W, local, tt, kb);
+    }
+}
+
 int main() {
   std::vector<int> Ts = {1, 2, 17, 31, 32, 33, 64, 100, 129, 200, 257, 300};
   std::vector<int> extra_S = {0, 1, 31, 63, 64, 160, 230};
@@ -107,9 +134,11 @@ int main() {
           check_query_blocked(T, S, W, local, 128, 32, 32);   // forward, d = 256, two heads per K/V head
           check_query_blocked(T, S, W, local, 256, 32, 32);   // forward, d = 256, one head per K/V head
           check_query_blocked(T, S, W, local, 128, 32, 64);   // forward, d <= 128
-          check_query_blocked(T, S, W, local, 32, 16, 32);    // dQ, two heads per K/V head
-          check_query_blocked(T, S, W, local, 64, 16, 32);    // dQ, one head per K/V head
+          check_query_blocked(T, S, W, local, 64, 64, 32);    // dQ, d = 256, two heads per K/V head
+          check_query_blocked(T, S, W, local, 128, 64, 32);   // dQ, d = 256 one head, d <= 128 two heads
+          check_query_blocked(T, S, W, local, 256, 64, 32);   // dQ, d <= 128, one head per K/V head
           check_key_blocked(T, S, W, local, 64, 16, 32);      // dK/dV
+          check_ds_blocks(T, S, W, local, 64);                // dS blocks between the two
           ++cases;
         }
   // the advisor's example: a chunked local layer whose first key block no row sees
