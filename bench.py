@@ -14,7 +14,8 @@ One step = the whole hot path on seeded synthetic inputs shaped like Gemma 2 9B:
   (30) over the prefill batch's vocabulary logits (2*8192 x 256000, bf16);
   and the backward pass of the 9B local+global pair (dq, dk, dv for a seeded
   upstream gradient), counted as 10*d FLOPs per visible (query head, key) pair
-  (S recomputed, dP, dV, dK, dQ); and the local + global prefill pairs of the
+  (S recomputed, dP, dV, dK, dQ: what its kernels execute, dS being stored
+  once rather than recomputed); and the local + global prefill pairs of the
   2B-shaped (B=4, H=8, KVH=4, d=256) and 27B-shaped (B=1, H=32, KVH=16,
   d=128, query_scale 1/12) workloads.
   Each of these secondary timings first runs its launches back to back for
@@ -243,7 +244,7 @@ def time_backward(g2, qd, kd, vd, kw, dev, stream, reps=5):
     tf = total_f / total_t / 1e12
     res.update({"metric": "backward eff. TFLOP/s (10*d per visible pair)", "value": round(tf, 2),
                 "unit": "TFLOP/s", "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                "executed_flops_per_pair": 14 * d, "flops": total_f})
+                "executed_flops_per_pair": 10 * d, "flops": total_f})
     return res
 
 
