@@ -142,29 +142,28 @@ def test_final_softcap_disabled_leaves_data(g2):
 
 # ---------------------------------------------- the sizes the benchmark times
 
-def test_rope_9b_full_size_sampled(g2):
-    """Q of the 9B layer (B=2, T=8192, 16 heads, d=256) at positions 0..T-1,
-    in place as the benchmark runs it; sampled rows against the oracle."""
+def test_rope_9b_full_size_whole_output(g2):
+    """Q (16 heads) and K (8 heads) of the 9B layer (B=2, T=8192, d=256) at
+    positions 0..T-1, in place as the benchmark runs it; every element against
+    the oracle, one batch entry at a time."""
     cfg = synth.WORKLOADS["9b-8k"]
-    B, T, H, d = cfg["B"], cfg["T"], cfg["H"], cfg["d"]
-    say("rope full 9b q")
-    q, _, _ = synth.prefill_inputs(cfg)
+    B, T, d = cfg["B"], cfg["T"], cfg["d"]
+    q, k, _ = synth.prefill_inputs(cfg)
     pos = torch.arange(T, dtype=torch.int32).repeat(B, 1).contiguous()
-    qd = q.cuda()
-    g2.rope_(qd, pos.cuda())
-    torch.cuda.synchronize()
-    rng = np.random.default_rng(51)
-    ts = sorted({0, 1, 2, 255, 4095, 4096, T - 2, T - 1, *rng.integers(0, T, 40).tolist()})
-    for b in range(B):
-        xs = synth.to_f32_numpy(q[b:b + 1, ts])                   # (1, n, H, d)
-        ps = np.asarray(ts, np.int32).reshape(1, -1)
-        ref = oracle.rope(xs, ps)
-        got = synth.to_f32_numpy(qd[b:b + 1, ts].cpu())
-        xn = xs.astype(np.float64)
-        h = d // 2
-        pair = np.abs(xn[..., :h]) + np.abs(xn[..., h:])
-        arith = 4.0 * 2.0 ** -24 * np.concatenate([pair, pair], axis=-1)
-        check_storage(got, ref, "bf16", f"rope full 9b batch {b}", arith=arith)
+    for name, x in (("q", q), ("k", k)):
+        say(f"rope full 9b {name}")
+        xd = x.cuda()
+        g2.rope_(xd, pos.cuda())
+        torch.cuda.synchronize()
+        for b in range(B):
+            xs = synth.to_f32_numpy(x[b:b + 1])                       # (1, T, NH, d)
+            ref = oracle.rope(xs, pos[b:b + 1].numpy())
+            got = synth.to_f32_numpy(xd[b:b + 1].cpu())
+            xn = xs.astype(np.float64)
+            h = d // 2
+            pair = np.abs(xn[..., :h]) + np.abs(xn[..., h:])
+            arith = 4.0 * 2.0 ** -24 * np.concatenate([pair, pair], axis=-1)
+            check_storage(got, ref, "bf16", f"rope full 9b {name} batch {b}", arith=arith)
 
 
 def test_final_softcap_full_size_sampled(g2):
