@@ -117,6 +117,27 @@ def test_entry_points_reject_before_launching():
                              _fake(0x10004), need, null) == ALIGN
 
 
+def test_backward_entry_point_rejects_before_launching():
+    """The backward's workspace (row statistics and dS blocks) is checked for
+    size and 16-byte alignment on the host, before anything is launched."""
+    lib = g2.lib
+    a, lse = _fake(0x10000), _fake(0x20000)
+    null = ctypes.c_void_p(0)
+    B, T, S, H, KVH, d = 1, 40, 70, 4, 2, 64
+    need = g2.backward_workspace_bytes(B, T, S, H)
+
+    def call(ws, nbytes, lse_ptr=lse, bf16=0):
+        return lib.g2attn_prefill_backward(a, a, a, a, a, lse_ptr, a, a, a, B, T, S, H, KVH, d,
+                                           0.125, 50.0, 16, 1, bf16, ws, nbytes, null)
+
+    assert call(null, need) == WS
+    assert call(a, need - 1) == WS
+    assert call(_fake(0x10008), need) == ALIGN          # 8-byte aligned workspace
+    assert call(a, need, lse_ptr=_fake(0x20002)) == ALIGN
+    assert call(a, need, bf16=1) == UNSUP                # the backward is bf16 only
+    assert lib.g2attn_prefill_backward_workspace_bytes(B, T, T - 1, H) == 0   # S < T
+
+
 def test_binding_requires_gpu_tensors():
     import torch
     q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
