@@ -117,6 +117,11 @@ int g2attn_prefill_lse(const void* q, const void* k, const void* v, void* out,
  * that the dK/dV kernel stores and the dQ kernel reads, about 2 B T S H bytes
  * in all (4.3 GB for B = 2, T = S = 8192, H = 16).  Buffers may not alias
  * each other.  G2_ERR_WORKSPACE if the workspace is missing or too small.
+ * To bound the workspace on long contexts, call it per chunk of query rows:
+ * rows [t0, t1) passed as q, out, dout and lse sliced to those rows against
+ * the first t1 keys (S = t1) sit at their own positions, and give those
+ * rows' dq and their rows' share of dk and dv (for keys below t1); the shares
+ * summed over the chunks are the layer's dk and dv.
  */
 int g2attn_prefill_backward(const void* q, const void* k, const void* v,
                             const void* out, const void* dout, const float* lse,

@@ -176,6 +176,43 @@ def test_backward_window_int_max_equals_global(g2, chunk):
 
 
 @pytest.mark.parametrize("is_local", [True, False], ids=["local", "global"])
+def test_backward_by_query_chunks(g2, is_local):
+    """A backward with bounded workspace: rows [t0, t1) of a T = S layer are
+    passed as a chunk (q, out, dO and lse sliced to those rows) against the
+    first t1 keys (S = t1), where bottom-right alignment puts them at their own
+    positions.  Each chunk gives its rows' dq and its rows' share of dk and dv;
+    the shares summed over the chunks are the layer's gradients (oracle), and
+    each chunk's workspace is that of its own (T, S) only."""
+    B, T, H, KVH, d, W = 1, 1000, 4, 2, 128, 300
+    say(f"backward by query chunks {'local' if is_local else 'global'}")
+    q = synth.draw((B, T, H, d), 951, 0, mul=3.0)
+    k = synth.draw((B, T, KVH, d), 951, 1, mul=3.0)
+    v = synth.draw((B, T, KVH, d), 951, 2)
+    dout = synth.draw((B, T, H, d), 951, 3)
+    kw = dict(query_scale=d ** -0.5, softcap=50.0, window=W, is_local=is_local)
+    qd, kd, vd, gd = q.cuda(), k.cuda(), v.cuda(), dout.cuda()
+    out, lse = g2.prefill_lse(qd, kd, vd, **kw)
+    dq = torch.empty_like(qd)
+    dk = torch.zeros(kd.shape, dtype=torch.float32, device="cuda")
+    dv = torch.zeros_like(dk)
+    bounds = [0, 352, 700, T]
+    for t0, t1 in zip(bounds[:-1], bounds[1:]):
+        rows = slice(t0, t1)
+        cq, ck, cv = qd[:, rows].contiguous(), kd[:, :t1].contiguous(), vd[:, :t1].contiguous()
+        ws = torch.empty(g2.backward_workspace_bytes(B, t1 - t0, t1, H), dtype=torch.uint8, device="cuda")
+        gq, gk, gv = g2.prefill_backward(cq, ck, cv, out[:, rows].contiguous(), gd[:, rows].contiguous(),
+                                         lse[:, :, rows].contiguous(), workspace=ws, **kw)
+        dq[:, rows] = gq
+        dk[:, :t1] += gk.float()
+        dv[:, :t1] += gv.float()
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.prefill_backward(*(synth.to_f32_numpy(x) for x in (q, k, v, dout)), **kw)
+    check_grad(synth.to_f32_numpy(dq), rq, f"dq by chunks {'local' if is_local else 'global'}")
+    check_grad(dk.cpu().numpy(), rk, f"dk by chunks {'local' if is_local else 'global'}")
+    check_grad(dv.cpu().numpy(), rv, f"dv by chunks {'local' if is_local else 'global'}")
+
+
+@pytest.mark.parametrize("is_local", [True, False], ids=["local", "global"])
 def test_backward_9b_heads_1k(g2, is_local):
     """The 9B head layout (H=16, KVH=8, d=256) at 1024 positions, window 256."""
     B, T, H, KVH, d, W = 1, 1024, 16, 8, 256, 256
